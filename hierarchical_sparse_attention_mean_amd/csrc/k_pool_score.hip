@@ -1,0 +1,260 @@
+// Fused pyramid pooling + scoring: one pass over Q, K and V.
+//
+// "Long Context Pre-Training with Lighthouse Attention":
+//   Sec. 3.3  level l entry i is the mean of Q (and K, V alike) over the base
+//             window [i p^l, (i+1) p^l - 1];
+//   Sec. 3.4  level-0 scores are the per-head l2 norms ||Q_t|| (query score QK)
+//             and ||K_t|| (key score KQ); coarser levels take the max of the
+//             level-0 scores over their window.
+// For every candidate entry (levels 0..L-2) the kernel also writes the 64-bit
+// selection key used by the top-k:
+//   key = bits(max(QK, KQ)) << 32 | (0xFFFFFFFF - g),
+// g = f if QK >= KQ else P + f (stream index of the larger score; f = flat
+// index).  Scores are non-negative, so the float bits order like the values,
+// and "larger key" means "larger score, then lower stream index": the order of
+// the joint selection over the concatenated QK || KQ stream.
+//
+// Work mapping: a work-group of 256 threads covers RG row-groups x CH column
+// chunks (8 elements each).  Row-group rg owns one coarsest window of
+// G = p^(L-1) consecutive rows and walks it top to bottom, so every pooled
+// window and every max-pool lives in one thread's registers; only the norm of a
+// row needs a reduction, across the CH lanes that hold it (adjacent lanes of one
+// wavefront, reduced with xor shuffles).
+#include "lh_internal.h"
+
+namespace lh {
+
+namespace {
+
+constexpr int kMaxL = 8;   // most levels handled by the register-resident accumulators
+
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float *p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float *p, const float (&x)[8]) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+template <> struct Vec8<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float (&x)[8]) {
+    const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
+    const unsigned int w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t *p, const float (&x)[8]) {
+    unsigned int w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned int)f32_to_bf16_rne(x[2 * i]) | ((unsigned int)f32_to_bf16_rne(x[2 * i + 1]) << 16);
+    reinterpret_cast<uint4 *>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+__device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f, int P) {
+  const float r = fmaxf(qk, kq);
+  const unsigned int g = (qk >= kq) ? (unsigned int)f : (unsigned int)(P + f);
+  return ((unsigned long long)__float_as_uint(r) << 32) | (unsigned long long)(0xFFFFFFFFu - g);
+}
+
+template <typename T, int D, int ML>
+__global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict__ q, const T *__restrict__ k,
+                                                    const T *__restrict__ v, char *__restrict__ ws, FwdWs w,
+                                                    float *__restrict__ scores) {
+  constexpr int CH = D / 8;          // threads per row
+  constexpr int RG = 256 / CH;       // row-groups per work-group
+  const int h = blockIdx.y;
+  const int j = threadIdx.x % CH;
+  const int rg = threadIdx.x / CH;
+  const int L = s.L;
+  const int G = s.pw[L - 1];
+  const long long win = (long long)blockIdx.x * RG + rg;   // coarsest window index
+  const bool active = win < s.n[L - 1];
+  const int P = s.P;
+
+  const long long hoff = (long long)h * s.N * D;
+  float *sc_qk = scores + (long long)h * 2 * P;
+  float *sc_kq = sc_qk + P;
+  unsigned long long *keys = reinterpret_cast<unsigned long long *>(ws + w.keys) + (long long)h * s.E;
+
+  // running window sums and max-pooled scores per level l >= 1 (ML >= L levels)
+  float aq[ML][8], ak[ML][8], av[ML][8];
+  float ma[ML], mb[ML];
+#pragma unroll
+  for (int l = 0; l < ML; ++l) {
+    ma[l] = 0.f;
+    mb[l] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
+  }
+  unsigned int umin = 0xFFFFFFFFu, umax = 0u;
+
+  const long long t0 = win * G;
+  for (int r = 0; r < G; ++r) {
+    const long long t = t0 + r;
+    float xq[8], xk[8], xv[8];
+    if (active) {
+      Vec8<T>::load(q + hoff + t * D + j * 8, xq);
+      Vec8<T>::load(k + hoff + t * D + j * 8, xk);
+      Vec8<T>::load(v + hoff + t * D + j * 8, xv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.f;
+    }
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq = fmaf(xq[e], xq[e], sq);
+      sk = fmaf(xk[e], xk[e], sk);
+    }
+#pragma unroll
+    for (int m = 1; m < CH; m <<= 1) {
+      sq += __shfl_xor(sq, m, CH);
+      sk += __shfl_xor(sk, m, CH);
+    }
+    const float a = sqrtf(sq);
+    const float b = sqrtf(sk);
+    if (active && j == 0) {
+      sc_qk[t] = a;
+      sc_kq[t] = b;
+      if (L > 1) {
+        const unsigned long long key = make_key(a, b, (int)t, P);
+        keys[t] = key;
+        const unsigned int hi = (unsigned int)(key >> 32);
+        umin = min(umin, hi);
+        umax = max(umax, hi);
+      }
+    }
+    if (L == 1) continue;
+    // level 1 accumulates rows; level l+1 accumulates completed level-l windows
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      aq[1][e] += xq[e];
+      ak[1][e] += xk[e];
+      av[1][e] += xv[e];
+    }
+    ma[1] = fmaxf(ma[1], a);
+    mb[1] = fmaxf(mb[1], b);
+#pragma unroll
+    for (int l = 1; l < ML; ++l) {
+      if (l >= L) break;
+      if (((r + 1) % s.pw[l]) != 0) break;   // window of level l not complete yet
+      const long long i = (t + 1) / s.pw[l] - 1;
+      const float inv = 1.0f / (float)s.pw[l];
+      if (active) {
+        float mq[8], mk[8], mv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mq[e] = aq[l][e] * inv;
+          mk[e] = ak[l][e] * inv;
+          mv[e] = av[l][e] * inv;
+        }
+        const long long lo = ((long long)h * s.n[l] + i) * D + j * 8;
+        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][0]) + lo, mq);
+        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][1]) + lo, mk);
+        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][2]) + lo, mv);
+        if (j == 0) {
+          const int f = s.off[l] + (int)i;
+          sc_qk[f] = ma[l];
+          sc_kq[f] = mb[l];
+          if (l <= L - 2) {
+            const unsigned long long key = make_key(ma[l], mb[l], f, P);
+            keys[f] = key;
+            const unsigned int hi = (unsigned int)(key >> 32);
+            umin = min(umin, hi);
+            umax = max(umax, hi);
+          }
+        }
+      }
+      if (l + 1 < ML && l + 1 < L) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          aq[l + 1][e] += aq[l][e];
+          ak[l + 1][e] += ak[l][e];
+          av[l + 1][e] += av[l][e];
+        }
+        ma[l + 1] = fmaxf(ma[l + 1], ma[l]);
+        mb[l + 1] = fmaxf(mb[l + 1], mb[l]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
+      ma[l] = 0.f;
+      mb[l] = 0.f;
+    }
+  }
+  if (L == 1) return;
+  // score-bit range of the candidates, for the top-k histogram
+  __shared__ unsigned int red_min[256], red_max[256];
+  red_min[threadIdx.x] = umin;
+  red_max[threadIdx.x] = umax;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) {
+      red_min[threadIdx.x] = min(red_min[threadIdx.x], red_min[threadIdx.x + st]);
+      red_max[threadIdx.x] = max(red_max[threadIdx.x], red_max[threadIdx.x + st]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && red_min[0] <= red_max[0]) {
+    TopkState *stt = reinterpret_cast<TopkState *>(ws + w.state) + h;
+    atomicMin(&stt->umin, red_min[0]);
+    atomicMax(&stt->umax, red_max[0]);
+  }
+}
+
+__global__ void k_fill_u32(unsigned int *p, size_t n, unsigned int value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(void *p, size_t n_u32, unsigned int value, hipStream_t st) {
+  if (n_u32 == 0) return hipSuccess;
+  size_t blocks = (n_u32 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(reinterpret_cast<unsigned int *>(p), n_u32, value);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *k, const void *v, char *ws,
+                          const FwdWs &w, float *scores, hipStream_t st) {
+  const T *qq = (const T *)q, *kk = (const T *)k, *vv = (const T *)v;
+  if (s.L <= 2)
+    k_pool_score<T, D, 2><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+  else if (s.L == 3)
+    k_pool_score<T, D, 3><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+  else if (s.L == 4)
+    k_pool_score<T, D, 4><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+  else
+    k_pool_score<T, D, kMaxL><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+}
+
+hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
+                             const FwdWs &w, float *scores, hipStream_t st) {
+  if (s.L > kMaxL) return hipErrorInvalidValue;
+  const int CH = s.d / 8;
+  const int RG = 256 / CH;
+  const int nwin = s.n[s.L - 1];
+  dim3 grid((nwin + RG - 1) / RG, s.BH);
+  char *wsb = reinterpret_cast<char *>(ws);
+  if (s.io == LH_BF16) {
+    if (s.d == 128) pool_score_ml<uint16_t, 128>(s, grid, q, k, v, wsb, w, scores, st);
+    else pool_score_ml<uint16_t, 64>(s, grid, q, k, v, wsb, w, scores, st);
+  } else {
+    if (s.d == 128) pool_score_ml<float, 128>(s, grid, q, k, v, wsb, w, scores, st);
+    else pool_score_ml<float, 64>(s, grid, q, k, v, wsb, w, scores, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lh

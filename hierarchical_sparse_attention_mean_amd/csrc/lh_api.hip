@@ -1,0 +1,315 @@
+// C ABI of liblighthouse.so: argument validation, buffer layouts and the launch
+// sequence of the Lighthouse layer ("Long Context Pre-Training with Lighthouse
+// Attention", Sec. 3.2-3.6).  Nothing here allocates, frees or synchronises;
+// every call only enqueues kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "lh_internal.h"
+
+namespace lh {
+hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+                                float *ot, float *lse, hipStream_t st);
+hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+                                const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
+                                float *dkt, float *dvt, hipStream_t st);
+}  // namespace lh
+
+namespace {
+
+thread_local std::string g_err;
+
+lh_status fail(lh_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+lh_status fail(lh_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(int dt) { return dt == LH_BF16 ? 2 : 4; }
+
+// Validates the shape and fills `s`.  Host-only.
+lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io, lh::Shape *s) {
+  memset(s, 0, sizeof *s);
+  if (B < 1 || H < 1) return fail(LH_EINVAL, "B and H must be >= 1 (got B=%d H=%d)", B, H);
+  if ((int64_t)B * H > (1 << 20)) return fail(LH_EUNSUPPORTED, "B*H too large");
+  if (N < 1) return fail(LH_EINVAL, "N must be >= 1 (got %lld)", (long long)N);
+  if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
+  if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
+  if (L < 1) return fail(LH_EINVAL, "L must be >= 1 (got %d)", L);
+  if (L > 8) return fail(LH_EUNSUPPORTED, "L must be <= 8 (got %d)", L);
+  if (p < 2) return fail(LH_EINVAL, "p must be >= 2 (got %d)", p);
+  if (topk < 0) return fail(LH_EINVAL, "topk must be >= 0 (got %lld)", (long long)topk);
+  if (N * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "N*d must be < 2^31");
+  int64_t pw = 1;
+  for (int l = 0; l < L; ++l) {
+    if (l > 0) pw *= p;
+    if (pw > N) return fail(LH_EDIVIS, "p^(L-1) = %d^%d exceeds N = %lld", p, L - 1, (long long)N);
+  }
+  if (N % pw != 0)
+    return fail(LH_EDIVIS, "p^(L-1) = %lld must divide N = %lld", (long long)pw, (long long)N);
+  s->BH = B * H;
+  s->N = (int)N;
+  s->d = d;
+  s->L = L;
+  s->p = p;
+  s->io = io;
+  s->topk = topk;
+  int64_t acc = 0, w = 1;
+  for (int l = 0; l < L; ++l) {
+    s->pw[l] = (int)w;
+    s->n[l] = (int)(N / w);
+    s->off[l] = (int)acc;
+    acc += N / w;
+    w *= p;
+  }
+  s->P = (int)acc;
+  s->E = (int)(acc - s->n[L - 1]);
+  // budget (L-1) p k, saturating, capped by the candidates
+  int64_t budget = s->E;
+  if (topk < ((int64_t)1 << 40)) {
+    const int64_t b = (int64_t)(L - 1) * p * topk;
+    if (b < budget) budget = b;
+  }
+  s->Bsel = (int)budget;
+  s->S = s->n[L - 1] + s->Bsel;
+  if ((int64_t)s->S * d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
+  s->ntile = (s->N + lh::kCompactTile - 1) / lh::kCompactTile;
+  return LH_OK;
+}
+
+void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
+  const size_t BH = (size_t)s.BH, P = (size_t)s.P, S = (size_t)s.S, d = (size_t)s.d;
+  const size_t es = elem_size(s.io);
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  o->scores = take(4 * BH * 2 * P);
+  o->flags = take(BH * P);
+  o->slot = take(4 * BH * P);
+  o->coords = take(4 * BH * S);
+  o->qt = take(es * BH * S * d);
+  o->kt = take(es * BH * S * d);
+  o->vt = take(es * BH * S * d);
+  o->vtt = take(es * BH * S * d);
+  o->ot = take(4 * BH * S * d);
+  o->lse = take(4 * BH * S);
+  o->total = cur;
+  o->P = s.P;
+  o->E = s.E;
+  o->Bsel = s.Bsel;
+  o->S = s.S;
+}
+
+void fwd_ws_layout(const lh::Shape &s, lh::FwdWs *w) {
+  const size_t BH = (size_t)s.BH, d = (size_t)s.d, es = elem_size(s.io);
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  memset(w, 0, sizeof *w);
+  for (int l = 1; l < s.L; ++l)
+    for (int t = 0; t < 3; ++t) w->lev[l][t] = take(es * BH * (size_t)s.n[l] * d);
+  w->keys = take(8 * BH * (size_t)s.E);
+  // state and histogram are adjacent: one fill kernel clears both
+  w->state = take(sizeof(lh::TopkState) * BH);
+  w->hist = cur;
+  cur = align_up(cur + 4 * BH * lh::kHistBins);
+  w->cand = take(8 * BH * (size_t)s.E);
+  w->tilecount = take(4 * BH * (size_t)s.ntile);
+  w->total = cur;
+}
+
+void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
+  const size_t BH = (size_t)s.BH, S = (size_t)s.S, d = (size_t)s.d;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  w->dot = take(4 * BH * S * d);
+  w->delta = take(4 * BH * S);
+  w->dqt = take(4 * BH * S * d);
+  w->dkt = take(4 * BH * S * d);
+  w->dvt = take(4 * BH * S * d);
+  w->total = cur;
+}
+
+lh_status hip_check(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(LH_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return LH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lh_status_string(lh_status s) {
+  switch (s) {
+    case LH_OK: return "ok";
+    case LH_EINVAL: return "invalid argument";
+    case LH_EDIVIS: return "p^(L-1) does not divide N";
+    case LH_EUNSUPPORTED: return "unsupported shape or dtype";
+    case LH_EWORKSPACE: return "buffer too small";
+    case LH_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *lh_last_error(void) { return g_err.c_str(); }
+
+lh_status lh_query(int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io, int64_t *S,
+                   size_t *saved_bytes, size_t *fwd_ws_bytes, size_t *bwd_ws_bytes) {
+  lh::Shape s;
+  lh_status st = make_shape(B, H, N, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  lh_saved_layout_t sl;
+  saved_layout(s, &sl);
+  lh::FwdWs fw;
+  fwd_ws_layout(s, &fw);
+  lh::BwdWs bw;
+  bwd_ws_layout(s, &bw);
+  if (S) *S = s.S;
+  if (saved_bytes) *saved_bytes = sl.total;
+  if (fwd_ws_bytes) *fwd_ws_bytes = fw.total;
+  if (bwd_ws_bytes) *bwd_ws_bytes = bw.total;
+  return LH_OK;
+}
+
+lh_status lh_saved_layout(int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io,
+                          lh_saved_layout_t *out) {
+  if (!out) return fail(LH_EINVAL, "out is NULL");
+  lh::Shape s;
+  lh_status st = make_shape(B, H, N, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  saved_layout(s, out);
+  return LH_OK;
+}
+
+lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dtype o_dtype, int B, int H, int64_t N,
+                     int d, int L, int p, int64_t topk, lh_dtype io, void *saved, size_t saved_bytes, void *ws,
+                     size_t ws_bytes, void *stream) {
+  lh::Shape s;
+  lh_status st = make_shape(B, H, N, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  if (o_dtype != LH_F32 && o_dtype != LH_BF16) return fail(LH_EINVAL, "o_dtype must be LH_F32 or LH_BF16");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(LH_EINVAL, "q, k, v, o must be non-NULL and 16-byte aligned");
+  if (!aligned16(saved) || !aligned16(ws)) return fail(LH_EINVAL, "saved and ws must be non-NULL and 16-byte aligned");
+  lh_saved_layout_t sl;
+  saved_layout(s, &sl);
+  lh::FwdWs fw;
+  fwd_ws_layout(s, &fw);
+  if (saved_bytes < sl.total)
+    return fail(LH_EWORKSPACE, "saved buffer too small: %zu < %zu bytes", saved_bytes, sl.total);
+  if (ws_bytes < fw.total) return fail(LH_EWORKSPACE, "forward workspace too small: %zu < %zu bytes", ws_bytes, fw.total);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  char *sv = reinterpret_cast<char *>(saved);
+  float *scores = reinterpret_cast<float *>(sv + sl.scores);
+  uint8_t *flags = reinterpret_cast<uint8_t *>(sv + sl.flags);
+  int *slot = reinterpret_cast<int *>(sv + sl.slot);
+  int *coords = reinterpret_cast<int *>(sv + sl.coords);
+  float *ot = reinterpret_cast<float *>(sv + sl.ot);
+  float *lse = reinterpret_cast<float *>(sv + sl.lse);
+
+  // (ii) top-k state (umin = ~0, the rest 0) and histogram cleared by a kernel
+  if ((st = hip_check(lh::launch_topk_init(s, ws, fw, hs), "topk_init")) != LH_OK) return st;
+  // (i)+(ii) pyramid and scores in one pass over Q, K, V
+  if ((st = hip_check(lh::launch_pool_score(s, q, k, v, ws, fw, scores, hs), "pool_score")) != LH_OK) return st;
+  // (ii) selection
+  if ((st = hip_check(lh::launch_topk(s, ws, fw, flags, hs), "topk")) != LH_OK) return st;
+  // (iii) topological compaction + gather
+  if ((st = hip_check(lh::launch_compact_gather(s, q, k, v, ws, fw, flags, slot, coords, sv + sl.qt, sv + sl.kt,
+                                                sv + sl.vt, sv + sl.vtt, hs),
+                      "compact_gather")) != LH_OK)
+    return st;
+  // (iii) causal attention over the sub-sequence
+  hipError_t e;
+  e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
+  if ((st = hip_check(e, "attention")) != LH_OK) return st;
+  // (iv) scatter-back
+  if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
+  return LH_OK;
+}
+
+lh_status lh_backward(const void *q, const void *k, const void *v, const void *dout, lh_dtype dout_dtype,
+                      const void *saved, size_t saved_bytes, void *dq, void *dk, void *dv, lh_dtype grad_dtype, int B,
+                      int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io, void *ws, size_t ws_bytes,
+                      void *stream) {
+  lh::Shape s;
+  lh_status st = make_shape(B, H, N, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  if (dout_dtype != LH_F32 && dout_dtype != LH_BF16) return fail(LH_EINVAL, "dout_dtype must be LH_F32 or LH_BF16");
+  if (grad_dtype != LH_F32 && grad_dtype != LH_BF16) return fail(LH_EINVAL, "grad_dtype must be LH_F32 or LH_BF16");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout))
+    return fail(LH_EINVAL, "q, k, v, dout must be non-NULL and 16-byte aligned");
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(LH_EINVAL, "dq, dk, dv must be non-NULL and 16-byte aligned");
+  if (!aligned16(saved) || !aligned16(ws)) return fail(LH_EINVAL, "saved and ws must be non-NULL and 16-byte aligned");
+  lh_saved_layout_t sl;
+  saved_layout(s, &sl);
+  lh::BwdWs bw;
+  bwd_ws_layout(s, &bw);
+  if (saved_bytes < sl.total)
+    return fail(LH_EWORKSPACE, "saved buffer too small: %zu < %zu bytes", saved_bytes, sl.total);
+  if (ws_bytes < bw.total) return fail(LH_EWORKSPACE, "backward workspace too small: %zu < %zu bytes", ws_bytes, bw.total);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const char *sv = reinterpret_cast<const char *>(saved);
+  char *wb = reinterpret_cast<char *>(ws);
+  const int *slot = reinterpret_cast<const int *>(sv + sl.slot);
+  const int *coords = reinterpret_cast<const int *>(sv + sl.coords);
+  const float *ot = reinterpret_cast<const float *>(sv + sl.ot);
+  const float *lse = reinterpret_cast<const float *>(sv + sl.lse);
+  float *dot = reinterpret_cast<float *>(wb + bw.dot);
+  float *delta = reinterpret_cast<float *>(wb + bw.delta);
+  float *dqt = reinterpret_cast<float *>(wb + bw.dqt);
+  float *dkt = reinterpret_cast<float *>(wb + bw.dkt);
+  float *dvt = reinterpret_cast<float *>(wb + bw.dvt);
+  (void)q;
+  (void)k;
+  (void)v;
+  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, slot, coords, dot, hs), "scatter_bwd")) != LH_OK)
+    return st;
+  hipError_t e;
+  e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
+                               dkt, dvt, hs);
+  if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  if ((st = hip_check(lh::launch_pool_bwd(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype, hs), "pool_bwd")) != LH_OK)
+    return st;
+  return LH_OK;
+}
+
+lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse, int BH, int64_t S,
+                               int d, lh_dtype io, void *stream) {
+  if (BH < 1 || S < 1) return fail(LH_EINVAL, "BH and S must be >= 1");
+  if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
+  if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
+  if (S * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(LH_EINVAL, "q, k, vt, o must be non-NULL and 16-byte aligned");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be 4-byte aligned");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, q, k, vt, o, lse, hs);
+  return hip_check(e, "attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal declarations shared by the HIP sources of liblighthouse.so.
+// Shape arithmetic follows "Long Context Pre-Training with Lighthouse
+// Attention": pyramid levels (Sec. 3.3), selection budget and sub-sequence
+// length (Sec. 3.5, Eq. 8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lighthouse.h"
+
+#define LH_MAX_LEVELS 24
+
+namespace lh {
+
+// Everything a kernel needs to know about one problem; passed by value.
+struct Shape {
+  int BH;                    // heads (B*H), processed independently
+  int N;                     // base positions per head
+  int d;                     // head dimension
+  int L, p;                  // levels, pooling factor
+  int io;                    // lh_dtype of q, k, v and of the pyramid / gathered rows
+  int64_t topk;
+  int n[LH_MAX_LEVELS];      // entries of level l: N / p^l
+  int off[LH_MAX_LEVELS];    // flat offset of level l (level-major, finest first)
+  int pw[LH_MAX_LEVELS];     // p^l
+  int P;                     // pyramid entries per head
+  int E;                     // candidates per head (levels 0..L-2)
+  int Bsel;                  // selected candidates per head
+  int S;                     // gathered length per head
+  int ntile;                 // compaction tiles per head
+};
+
+constexpr int kCompactTile = 1024;   // base positions per compaction work-group
+constexpr int kHistBins = 4096;      // first radix-select digit of the top-k
+constexpr int kTopkCandLds = 8192;   // candidates sorted in LDS by the bitonic stage
+
+// Per-head state of the top-k (in the forward workspace).
+struct TopkState {
+  unsigned int umin;        // min over candidates of the score bits (upper key half)
+  unsigned int umax;        // max of the same
+  unsigned int cand_count;  // keys in the boundary histogram bin
+  unsigned int bstar;       // boundary bin
+  long long need;           // keys still to take from the boundary bin
+  long long pad;
+};
+
+// Forward workspace layout (byte offsets).
+struct FwdWs {
+  size_t lev[LH_MAX_LEVELS][3];  // pooled Q, K, V of level l >= 1 ([BH][n_l][d], io dtype)
+  size_t keys;                   // uint64 [BH][E]
+  size_t state;                  // TopkState [BH]
+  size_t hist;                   // uint32 [BH][kHistBins]
+  size_t cand;                   // uint64 [BH][E]
+  size_t tilecount;              // int32 [BH][ntile]
+  size_t total;
+};
+
+// Backward workspace layout.
+struct BwdWs {
+  size_t dot;     // fp32 [BH][S][d]  gradient of O~
+  size_t delta;   // fp32 [BH][S]     rowsum(dO~ * O~)
+  size_t dqt;     // fp32 [BH][S][d]
+  size_t dkt;     // fp32 [BH][S][d]
+  size_t dvt;     // fp32 [BH][S][d]
+  size_t total;
+};
+
+// ---- bf16 helpers (storage is raw uint16 bit patterns) ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((unsigned int)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  unsigned int u = __float_as_uint(f);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint16_t)u;
+}
+
+template <typename T> struct IO;
+template <> struct IO<float> {
+  static __device__ __forceinline__ float ld(const float *p, long long i) { return p[i]; }
+  static __device__ __forceinline__ void st(float *p, long long i, float v) { p[i] = v; }
+};
+template <> struct IO<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t *p, long long i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void st(uint16_t *p, long long i, float v) { p[i] = f32_to_bf16_rne(v); }
+};
+
+// ---- launchers (each enqueues on `st`, returns hipGetLastError()) ----
+hipError_t launch_fill_u32(void *p, size_t n_u32, unsigned int value, hipStream_t st);
+hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
+                             const FwdWs &w, float *scores, hipStream_t st);
+hipError_t launch_topk_init(const Shape &s, void *ws, const FwdWs &w, hipStream_t st);
+hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, uint8_t *flags, hipStream_t st);
+hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
+                                 const FwdWs &w, const uint8_t *flags, int *slot, int *coords,
+                                 void *qt, void *kt, void *vt, void *vtt, hipStream_t st);
+hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void *o, int o_dtype,
+                          hipStream_t st);
+hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *slot,
+                              const int *coords, float *dot, hipStream_t st);
+hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, const float *dkt,
+                           const float *dvt, void *dq, void *dk, void *dv, int grad_dtype, hipStream_t st);
+
+}  // namespace lh

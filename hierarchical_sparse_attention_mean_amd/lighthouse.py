@@ -1,0 +1,242 @@
+"""ctypes binding of liblighthouse.so (the C ABI in include/lighthouse.h).
+
+The ``lh_*`` functions take the same arguments as their C counterparts, with
+torch tensors in place of device pointers; they only marshal arguments and
+return what the C call returns.  torch is used for device memory and the
+current stream, nothing else: every step of the layer runs in the library's
+HIP kernels.  The library must have been built (``build.py``); importing this
+module raises if it is missing.
+
+Convenience wrappers (``forward``, ``backward``, ``LighthouseAttention``)
+allocate the caller-owned buffers with torch and call the entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # noqa: F401  (must load torch's HIP runtime before the library)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "lighthouse.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_sparse_attention_mean_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+LH_F32, LH_BF16 = 0, 1
+STATUS = {0: "LH_OK", 1: "LH_EINVAL", 2: "LH_EDIVIS", 3: "LH_EUNSUPPORTED", 4: "LH_EWORKSPACE", 5: "LH_EHIP"}
+
+
+class LighthouseError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {lh_last_error()}")
+
+
+class SavedLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "ot", "lse", "total")] + \
+               [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S")]
+
+
+_i, _i64, _sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_P = ctypes.POINTER
+_lib.lh_query.argtypes = [_i, _i, _i64, _i, _i, _i, _i64, _i, _P(_i64), _P(_sz), _P(_sz), _P(_sz)]
+_lib.lh_query.restype = _i
+_lib.lh_saved_layout.argtypes = [_i, _i, _i64, _i, _i, _i, _i64, _i, _P(SavedLayout)]
+_lib.lh_saved_layout.restype = _i
+_lib.lh_forward.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i64, _i, _i, _i, _i64, _i, _vp, _sz, _vp, _sz, _vp]
+_lib.lh_forward.restype = _i
+_lib.lh_backward.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _sz, _vp, _vp, _vp, _i,
+                             _i, _i, _i64, _i, _i, _i, _i64, _i, _vp, _sz, _vp]
+_lib.lh_backward.restype = _i
+_lib.lh_attention_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp]
+_lib.lh_attention_forward.restype = _i
+_lib.lh_status_string.argtypes = [_i]
+_lib.lh_status_string.restype = ctypes.c_char_p
+_lib.lh_last_error.argtypes = []
+_lib.lh_last_error.restype = ctypes.c_char_p
+
+
+def library():
+    """The loaded ctypes library (for symbol checks)."""
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/lighthouse.h declares."""
+    with open(HEADER) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lh_[a-z_]+)\s*\(", txt)))
+
+
+def dtype_code(dt) -> int:
+    if dt in (torch.float32, "f32", LH_F32):
+        return LH_F32
+    if dt in (torch.bfloat16, "bf16", LH_BF16):
+        return LH_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# entry points, same names and arguments as the C ABI
+# ---------------------------------------------------------------------------
+def lh_status_string(status: int) -> str:
+    return _lib.lh_status_string(status).decode()
+
+
+def lh_last_error() -> str:
+    return _lib.lh_last_error().decode()
+
+
+def lh_query(B, H, N, d, L, p, topk, io):
+    """Returns (status, S, saved_bytes, fwd_ws_bytes, bwd_ws_bytes)."""
+    S, a, b, c = _i64(), _sz(), _sz(), _sz()
+    st = _lib.lh_query(B, H, N, d, L, p, topk, dtype_code(io), ctypes.byref(S), ctypes.byref(a),
+                       ctypes.byref(b), ctypes.byref(c))
+    return st, S.value, a.value, b.value, c.value
+
+
+def lh_saved_layout(B, H, N, d, L, p, topk, io):
+    """Returns (status, dict of byte offsets and sizes)."""
+    out = SavedLayout()
+    st = _lib.lh_saved_layout(B, H, N, d, L, p, topk, dtype_code(io), ctypes.byref(out))
+    return st, {n: getattr(out, n) for n, _ in SavedLayout._fields_}
+
+
+def lh_forward(q, k, v, o, o_dtype, B, H, N, d, L, p, topk, io, saved, saved_bytes, ws, ws_bytes, stream=None):
+    return _lib.lh_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(o_dtype), B, H, N, d, L, p, topk,
+                           dtype_code(io), _ptr(saved), saved_bytes, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def lh_backward(q, k, v, dout, dout_dtype, saved, saved_bytes, dq, dk, dv, grad_dtype, B, H, N, d, L, p, topk, io,
+                ws, ws_bytes, stream=None):
+    return _lib.lh_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dtype_code(dout_dtype), _ptr(saved),
+                            saved_bytes, _ptr(dq), _ptr(dk), _ptr(dv), dtype_code(grad_dtype), B, H, N, d, L, p,
+                            topk, dtype_code(io), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def lh_attention_forward(q, k, vt, o, lse, BH, S, d, io, stream=None):
+    return _lib.lh_attention_forward(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(lse), BH, S, d, dtype_code(io),
+                                     _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# convenience: torch-allocated buffers around the entry points
+# ---------------------------------------------------------------------------
+def _check(st, where):
+    if st != 0:
+        raise LighthouseError(st, where)
+
+
+def _shape(q):
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors")
+    return q.shape
+
+
+class Plan:
+    """Sizes and layouts for one (B, H, N, d, L, p, topk, io) problem."""
+
+    def __init__(self, B, H, N, d, L, p, topk, io):
+        self.B, self.H, self.N, self.d, self.L, self.p, self.topk = B, H, N, d, L, p, topk
+        self.io = dtype_code(io)
+        st, self.S, self.saved_bytes, self.fwd_ws_bytes, self.bwd_ws_bytes = lh_query(B, H, N, d, L, p, topk,
+                                                                                      self.io)
+        _check(st, "lh_query")
+        st, self.layout = lh_saved_layout(B, H, N, d, L, p, topk, self.io)
+        _check(st, "lh_saved_layout")
+
+    def args(self):
+        return (self.B, self.H, self.N, self.d, self.L, self.p, self.topk, self.io)
+
+
+def forward(q, k, v, L, p, topk, out_dtype=None, saved=None, ws=None, plan=None):
+    """O = Lighthouse(q, k, v).  Returns (o, saved, plan); `saved` feeds backward."""
+    B, H, N, d = _shape(q)
+    plan = plan or Plan(B, H, N, d, L, p, topk, q.dtype)
+    out_dtype = out_dtype or q.dtype
+    dev = q.device
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    if saved is None:
+        saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = torch.empty(plan.fwd_ws_bytes, dtype=torch.uint8, device=dev)
+    st = lh_forward(q, k, v, o, dtype_code(out_dtype), *plan.args()[:7], plan.io, saved, saved.numel(), ws,
+                    ws.numel())
+    _check(st, "lh_forward")
+    return o, saved, plan
+
+
+def backward(q, k, v, dout, saved, plan, grad_dtype=None, ws=None):
+    """(dq, dk, dv) with the forward's selection frozen."""
+    B, H, N, d = _shape(q)
+    grad_dtype = grad_dtype or q.dtype
+    dev = q.device
+    dq = torch.empty((B, H, N, d), dtype=grad_dtype, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    if ws is None:
+        ws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+    st = lh_backward(q, k, v, dout.contiguous(), dtype_code(dout.dtype), saved, saved.numel(), dq, dk, dv,
+                     dtype_code(grad_dtype), *plan.args()[:7], plan.io, ws, ws.numel())
+    _check(st, "lh_backward")
+    return dq, dk, dv
+
+
+def saved_view(saved, plan, name):
+    """Typed view of one array inside the saved buffer (see lighthouse.h)."""
+    lay = plan.layout
+    BH, P, S, d = plan.B * plan.H, lay["P"], lay["S"], plan.d
+    io = torch.bfloat16 if plan.io == LH_BF16 else torch.float32
+    spec = {
+        "scores": (torch.float32, (BH, 2, P)), "flags": (torch.uint8, (BH, P)), "slot": (torch.int32, (BH, P)),
+        "coords": (torch.int32, (BH, S)), "qt": (io, (BH, S, d)), "kt": (io, (BH, S, d)), "vt": (io, (BH, S, d)),
+        "vtt": (io, (BH, d, S)), "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
+    }[name]
+    dt, shape = spec
+    n = 1
+    for x in shape:
+        n *= x
+    nbytes = n * torch.tensor([], dtype=dt).element_size()
+    off = lay[name]
+    return saved[off:off + nbytes].view(dt).view(shape)
+
+
+class LighthouseAttention(torch.autograd.Function):
+    """autograd wrapper: forward and backward both run in liblighthouse."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, L, p, topk):
+        o, saved, plan = forward(q.contiguous(), k.contiguous(), v.contiguous(), L, p, topk)
+        ctx.save_for_backward(q, k, v, saved)
+        ctx.plan = plan
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, saved = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, do, saved, ctx.plan)
+        return dq, dk, dv, None, None, None

@@ -1,0 +1,136 @@
+/*
+ * lighthouse.h -- C ABI of the MI355X (gfx950) Lighthouse attention library.
+ *
+ * Lighthouse attention replaces causal scaled-dot-product attention on one
+ * head-batch by four stages ("Long Context Pre-Training with Lighthouse
+ * Attention", Sec. 3.2):
+ *   (i)   mean-pool Q, K and V alike into an L-level pyramid with factor p
+ *         (Sec. 3.3: window W_i^(l) = [i p^l, (i+1) p^l - 1], p^(L-1) | N);
+ *   (ii)  score every entry with per-head l2 norms (QK: ||Q||, KQ: ||K||), coarser
+ *         levels max-pooling the level-0 scores, and select jointly over both
+ *         streams and all levels (Sec. 3.4); the coarsest level is always kept;
+ *   (iii) gather the selected (Q, K, V) triples, sorted topologically by window
+ *         end, into a contiguous sub-sequence of length S and run plain causal
+ *         softmax attention over it (Sec. 3.5, Eq. 8 and Eq. 9);
+ *   (iv)  scatter each entry's output to the p^l base positions of its window
+ *         shifted by p^l - 1, summing the levels (Sec. 3.6), in deterministic
+ *         int64 fixed point (32 fractional bits, round-to-nearest-even).
+ * Selection budget: B = min((L-1) p k, |E|) distinct entries of the non-coarsest
+ * levels E, ranked by max(QK, KQ) with ties to the lowest stream index (QK score
+ * of flat entry f has stream index f, its KQ score |P| + f; flat index runs
+ * level-major, finest first).  S = N / p^(L-1) + B.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are [B, H, N, d] contiguous (d fastest), heads independent.  All
+ *    pointers are DEVICE pointers unless stated otherwise, 16-byte aligned.
+ *  - The caller owns and allocates every buffer; the library allocates, frees
+ *    and synchronises nothing.  Calls only enqueue work on `stream` (0 = the
+ *    null stream) and return; results are ready when the stream reaches them.
+ *  - Arguments are validated on the host before anything is enqueued: a call
+ *    that returns an error status has no side effects.  lh_last_error() then
+ *    gives a thread-local description.
+ *  - Inputs must be finite (NaN or Inf give undefined selections).
+ *  - Supported: d in {64, 128}; io dtype LH_F32 or LH_BF16 (bf16 storage, fp32
+ *    arithmetic, bf16 MFMA for the attention); L >= 1; p >= 2; topk >= 0.
+ *    topk larger than the candidates selects everything (S = |P|).
+ *  - No global mutable state except the thread-local error text: calls are
+ *    re-entrant; concurrent calls on different streams must use distinct
+ *    buffers.
+ */
+#ifndef LIGHTHOUSE_H
+#define LIGHTHOUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LH_F32 = 0, LH_BF16 = 1 } lh_dtype;
+
+typedef enum {
+  LH_OK = 0,
+  LH_EINVAL = 1,        /* null / misaligned pointer, non-positive size, bad enum */
+  LH_EDIVIS = 2,        /* p^(L-1) does not divide N */
+  LH_EUNSUPPORTED = 3,  /* d not in {64, 128}, or sizes beyond int32 indexing */
+  LH_EWORKSPACE = 4,    /* saved or workspace buffer smaller than lh_query says */
+  LH_EHIP = 5           /* a HIP launch failed; see lh_last_error() */
+} lh_status;
+
+/* Byte offsets of the arrays inside the `saved` buffer that lh_forward fills
+ * and lh_backward reads.  "BH" = B*H heads; P = pyramid entries per head;
+ * S = gathered length per head.  Exposed so tests can read intermediates. */
+typedef struct lh_saved_layout_t {
+  size_t scores;   /* fp32  [BH][2][P]  QK stream, then KQ stream (Sec. 3.4) */
+  size_t flags;    /* uint8 [BH][P]     1 = entry is in the index set I */
+  size_t slot;     /* int32 [BH][P]     position in the sub-sequence, -1 if not selected */
+  size_t coords;   /* int32 [BH][S]     flat pyramid index of the entry at each slot */
+  size_t qt;       /* io    [BH][S][d]  gathered Q~ (topological order) */
+  size_t kt;       /* io    [BH][S][d]  gathered K~ */
+  size_t vt;       /* io    [BH][S][d]  gathered V~ */
+  size_t vtt;      /* io    [BH][d][S]  V~ transposed (operand layout of the MFMA P.V product) */
+  size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
+  size_t lse;      /* fp32  [BH][S]     natural-log log-sum-exp of each O~ row's logits */
+  size_t total;    /* bytes needed */
+  int64_t P;       /* pyramid entries per head */
+  int64_t E;       /* candidate (non-coarsest) entries per head */
+  int64_t Bsel;    /* selected candidates per head */
+  int64_t S;       /* gathered length per head */
+} lh_saved_layout_t;
+
+/* Host-only.  Validates the shape and returns S and the byte sizes the caller
+ * must allocate: `saved` (forward -> backward state), and the forward and
+ * backward workspaces.  Any output pointer may be NULL.  (Sec. 3.3, 3.5.) */
+lh_status lh_query(int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io,
+                   int64_t *S, size_t *saved_bytes, size_t *fwd_ws_bytes, size_t *bwd_ws_bytes);
+
+/* Host-only.  Offsets of the arrays inside `saved` for this shape. */
+lh_status lh_saved_layout(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
+                          lh_dtype io, lh_saved_layout_t *out);
+
+/* Forward of the Lighthouse layer (Sec. 3.2, stages i-iv).
+ *   q, k, v : [B,H,N,d] in dtype `io` (read only).
+ *   o       : [B,H,N,d] output in dtype `o_dtype` (LH_F32 or LH_BF16); positions
+ *             with no selected contributor (t < p^(L-1) - 1 not covered by a
+ *             selected finer entry) are written as 0.
+ *   saved   : >= saved_bytes from lh_query; filled for lh_backward (layout above).
+ *   ws      : >= fwd_ws_bytes from lh_query; scratch, contents undefined after.
+ * Deterministic: equal inputs give bit-equal outputs. */
+lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dtype o_dtype,
+                     int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io,
+                     void *saved, size_t saved_bytes, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of the Lighthouse layer with the forward's selection frozen: the
+ * indices carry no gradient and nothing flows into the scores (Sec. 3.2).
+ *   dout       : [B,H,N,d] upstream gradient in dtype `dout_dtype`.
+ *   saved      : the buffer filled by lh_forward for the same q, k, v and shape.
+ *   dq, dk, dv : [B,H,N,d] gradients in dtype `grad_dtype` (overwritten).
+ *   ws         : >= bwd_ws_bytes from lh_query.
+ * Deterministic (no floating-point atomics). */
+lh_status lh_backward(const void *q, const void *k, const void *v, const void *dout,
+                      lh_dtype dout_dtype, const void *saved, size_t saved_bytes,
+                      void *dq, void *dk, void *dv, lh_dtype grad_dtype,
+                      int B, int H, int64_t N, int d, int L, int p, int64_t topk, lh_dtype io,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Dense causal softmax attention, softmax(Q K^T / sqrt(d) + causal) V, on given
+ * [BH,S,d] tensors (Sec. 3.1, Eq. 1): the kernel of stage (iii), exposed for the
+ * dense baseline at S = N.
+ *   q, k   : [BH][S][d] dtype `io`;  vt: V transposed [BH][d][S] for LH_BF16,
+ *            V itself [BH][S][d] for LH_F32.
+ *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
+lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,
+                               int BH, int64_t S, int d, lh_dtype io, void *stream);
+
+/* Text of a status code (static storage). */
+const char *lh_status_string(lh_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *lh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTHOUSE_H */

@@ -234,6 +234,24 @@ def attend(qt: np.ndarray, kt: np.ndarray, vt: np.ndarray, row_block: int = 1024
     return o, lse
 
 
+def attend_rows(qt: np.ndarray, kt: np.ndarray, vt: np.ndarray, rows):
+    """The rows ``rows`` of ``attend`` only (same per-row definition), for
+    checking sampled outputs of a sub-sequence too long to attend in full."""
+    S, d = qt.shape
+    scale = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), vt.shape[1]), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    for n, m in enumerate(rows):
+        z = (kt[:m + 1] @ qt[m]) * scale
+        zmax = z.max()
+        e = np.exp(z - zmax)
+        ssum = e.sum()
+        o[n] = (e / ssum) @ vt[:m + 1]
+        lse[n] = zmax + np.log(ssum)
+    return o, lse
+
+
 # ----------------------------------------------------------------------------
 # 7. scatter (Paper §3.6)
 # ----------------------------------------------------------------------------

@@ -1,0 +1,101 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes its buffers by the closed forms, and rejects bad
+arguments before enqueueing anything.  No kernel is launched here."""
+import ctypes
+
+import pytest
+
+import oracle as orc
+
+BIG = 1 << 40
+
+
+def test_exports_every_declared_symbol(lh):
+    names = lh.declared_symbols()
+    assert set(names) >= {"lh_query", "lh_forward", "lh_backward", "lh_attention_forward", "lh_saved_layout",
+                          "lh_status_string", "lh_last_error"}
+    lib = lh.library()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+@pytest.mark.parametrize("B,H,N,d,L,p,k,io", [
+    (1, 2, 1024, 64, 3, 4, 64, "f32"), (1, 8, 98304, 128, 3, 4, 768, "bf16"), (1, 8, 524288, 128, 3, 4, 4096, "bf16"),
+    (1, 8, 1048576, 128, 4, 4, 4096, "bf16"), (1, 8, 8192, 128, 3, 4, 64, "bf16"), (1, 2, 1024, 64, 3, 4, 1024, "f32"),
+    (2, 3, 96, 64, 1, 4, 5, "f32"), (1, 1, 1000000, 128, 4, 4, 4096, "bf16"), (1, 1, 64, 128, 4, 2, 0, "bf16")])
+def test_query_matches_closed_form(lh, B, H, N, d, L, p, k, io):
+    st, S, saved, fws, bws = lh.lh_query(B, H, N, d, L, p, k, io)
+    assert st == 0, lh.lh_last_error()
+    sizes = orc.level_sizes(N, L, p)
+    assert S == sizes[-1] + orc.budget(N, L, p, k)
+    st, lay = lh.lh_saved_layout(B, H, N, d, L, p, k, io)
+    assert st == 0
+    assert lay["S"] == S and lay["P"] == sum(sizes) and lay["E"] == sum(sizes[:-1])
+    es = 2 if io == "bf16" else 4
+    BH = B * H
+    order = ["scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "ot", "lse"]
+    need = {"scores": 8 * BH * lay["P"], "flags": BH * lay["P"], "slot": 4 * BH * lay["P"], "coords": 4 * BH * S,
+            "qt": es * BH * S * d, "kt": es * BH * S * d, "vt": es * BH * S * d, "vtt": es * BH * S * d,
+            "ot": 4 * BH * S * d, "lse": 4 * BH * S}
+    for a, b in zip(order, order[1:] + ["total"]):
+        assert lay[a] % 256 == 0
+        assert lay[b] - lay[a] >= need[a]           # arrays do not overlap
+    assert saved == lay["total"]
+    assert fws > 0 and bws >= 4 * BH * S * d * 4
+
+
+def test_page_example_S_through_abi(lh):
+    st, S, *_ = lh.lh_query(1, 1, 10 ** 6, 128, 4, 4, 4096, "bf16")
+    assert st == 0 and S == 64777
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 1000, 64, 3, 4, 8, "f32"), 2),       # 16 does not divide 1000
+    ((1, 1, 1024, 96, 3, 4, 8, "f32"), 3),       # d unsupported
+    ((1, 1, 1024, 64, 0, 4, 8, "f32"), 1),       # L < 1
+    ((1, 1, 1024, 64, 3, 1, 8, "f32"), 1),       # p < 2
+    ((1, 1, 1024, 64, 3, 4, -1, "f32"), 1),      # k < 0
+    ((0, 1, 1024, 64, 3, 4, 8, "f32"), 1),       # B < 1
+    ((1, 1, 0, 64, 3, 4, 8, "f32"), 1),          # N < 1
+    ((1, 1, 16, 64, 4, 4, 8, "f32"), 2),         # p^(L-1) > N
+    ((1, 1, 1 << 25, 128, 3, 4, 8, "f32"), 3),   # N*d >= 2^31
+])
+def test_query_rejects(lh, args, status):
+    st, *_ = lh.lh_query(*args)
+    assert st == status
+    assert lh.lh_last_error()
+    assert lh.lh_status_string(st) != "unknown status"
+
+
+def test_huge_topk_selects_everything(lh):
+    st, S, *_ = lh.lh_query(1, 1, 1024, 64, 3, 4, BIG, "f32")
+    assert st == 0 and S == 1344
+
+
+def test_forward_validation_before_launch(lh):
+    """Every one of these fails validation on the host; nothing is enqueued."""
+    B, H, N, d, L, p, k = 1, 2, 1024, 64, 3, 4, 64
+    st, S, saved, fws, bws = lh.lh_query(B, H, N, d, L, p, k, "f32")
+    fake = 1 << 20                     # aligned, never dereferenced
+    # null pointer
+    assert lh.lh_forward(None, fake, fake, fake, "f32", B, H, N, d, L, p, k, "f32", fake, saved, fake, fws) == 1
+    # misaligned pointer
+    assert lh.lh_forward(fake + 4, fake, fake, fake, "f32", B, H, N, d, L, p, k, "f32", fake, saved, fake, fws) == 1
+    # saved buffer too small
+    assert lh.lh_forward(fake, fake, fake, fake, "f32", B, H, N, d, L, p, k, "f32", fake, saved - 1, fake, fws) == 4
+    assert "saved" in lh.lh_last_error()
+    # workspace too small
+    assert lh.lh_forward(fake, fake, fake, fake, "f32", B, H, N, d, L, p, k, "f32", fake, saved, fake, fws - 1) == 4
+    # bad output dtype (raw call: the binding itself refuses unknown dtypes)
+    assert lh.library().lh_forward(fake, fake, fake, fake, 7, B, H, N, d, L, p, k, 0, fake, saved, fake, fws,
+                                   None) == 1
+    # divisibility is checked before anything else
+    assert lh.lh_forward(fake, fake, fake, fake, "f32", B, H, 1000, d, L, p, k, "f32", fake, saved, fake, fws) == 2
+    # backward: workspace too small, null gradient
+    assert lh.lh_backward(fake, fake, fake, fake, "f32", fake, saved, fake, fake, fake, "f32", B, H, N, d, L, p, k,
+                          "f32", fake, bws - 1) == 4
+    assert lh.lh_backward(fake, fake, fake, fake, "f32", fake, saved, None, fake, fake, "f32", B, H, N, d, L, p, k,
+                          "f32", fake, bws) == 1
+    # dense attention: unsupported d
+    assert lh.lh_attention_forward(fake, fake, fake, fake, None, 1, 128, 80, "bf16") == 3

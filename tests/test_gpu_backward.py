@@ -1,0 +1,104 @@
+"""GPU parity of the backward (selection frozen, indices carry no gradient).
+
+Two references, both the fp64 oracle with the GPU's selection injected:
+  * stage-consistent: the oracle's adjoints (scatter, attention, gather, pool)
+    evaluated on the GPU's own gathered rows, so only the kernels' arithmetic
+    differs -- bar 1e-3 of the gradient's largest magnitude (fp32 accumulation
+    over <= S terms, bf16 operands read exactly);
+  * end to end: the oracle's own fp64 pyramid and backward -- bar 2e-2 of the
+    gradient's largest magnitude, the forward's bf16 bar applied to the
+    gradients' scale (pooled rows are stored in bf16, so the logits of pooled
+    entries carry one bf16 rounding).
+At full size, properties that hold at any size: exact scaling by 2,
+run-to-run bit equality, finite values.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from gpu_helpers import bf16_tensor_to_f64, gpu_head, head_inputs_f64, run_forward, say, to_dev
+from hierarchical_sparse_attention_mean_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+STAGE_TOL = 1e-3
+E2E_TOL = 2e-2
+
+
+def _grads_stage_consistent(g, do64, N, L, p):
+    """Oracle adjoints on the GPU's own gathered rows."""
+    sf = g["coords"]
+    dot = orc.scatter_adjoint(do64, sf, N, L, p)
+    dqt, dkt, dvt = orc.attend_adjoint(g["qt"], g["kt"], g["vt"], dot)
+    lev, pos = orc.coords_of_flat(sf, N, L, p)
+    sizes = orc.level_sizes(N, L, p)
+    out = []
+    for dt in (dqt, dkt, dvt):
+        dl = [np.zeros((n, dt.shape[1])) for n in sizes]
+        for m in range(len(sf)):
+            dl[lev[m]][pos[m]] = dt[m]
+        out.append(orc.pool_adjoint(dl, N, p))
+    return out
+
+
+def _run_bwd(lh, cfg, heads, grad_dtype="f32"):
+    import torch
+    say(f"case bwd N={cfg['N']} H={cfg['H']} d={cfg['d']} L={cfg['L']} p={cfg['p']} k={cfg['k']} io={cfg['dtype']}")
+    inp = synth.make_inputs(cfg, with_do=True)
+    run = run_forward(lh, cfg, inp)
+    dout = to_dev(inp["do"], cfg["dtype"])
+    gdt = torch.float32 if grad_dtype == "f32" else torch.bfloat16
+    dq, dk, dv = lh.backward(run["q"], run["k"], run["v"], dout, run["saved"], run["plan"], grad_dtype=gdt)
+    torch.cuda.synchronize()
+    N, L, p, H = cfg["N"], cfg["L"], cfg["p"], cfg["H"]
+    for h in heads:
+        b, hh = divmod(h, H)
+        g = gpu_head(lh, run, h)
+        q64, k64, v64 = head_inputs_f64(cfg, inp, h)
+        do64 = synth.as_f64(inp["do"][b, hh], cfg["dtype"])
+        got = [bf16_tensor_to_f64(x[b, hh]) for x in (dq, dk, dv)]
+        ref_s = _grads_stage_consistent(g, do64, N, L, p)
+        ref_e = orc.backward_head(q64, k64, v64, do64, L, p, g["flags"])
+        for name, a, rs, re in zip(("dq", "dk", "dv"), got, ref_s, ref_e):
+            scale = np.max(np.abs(re))
+            es = np.max(np.abs(a - rs)) / scale
+            ee = np.max(np.abs(a - re)) / scale
+            say(f"  head {h} {name}: max|g|={scale:.3e} stage err={es:.3e} end-to-end err={ee:.3e}")
+            extra = 2.0 ** -8 if grad_dtype == "bf16" else 0.0
+            assert es <= STAGE_TOL + extra
+            assert ee <= E2E_TOL + extra
+    return run, dq, dk, dv
+
+
+def test_backward_tiny_fp32(lh):
+    _run_bwd(lh, synth.config("tiny"), heads=[0, 1])
+
+
+def test_backward_8k_bf16(lh):
+    _run_bwd(lh, synth.config("bwd8k"), heads=[0, 5])
+
+
+def test_backward_8k_select_all(lh):
+    """k = 4096 at N = 8192: every entry selected (S = |P|)."""
+    _run_bwd(lh, synth.config("bwd8k", k=4096, H=2), heads=[1])
+
+
+def test_backward_shapes(lh):
+    _run_bwd(lh, synth.config("tiny", N=2048, L=4, p=2, k=13, B=2, H=1, d=128), heads=[0, 1])
+    _run_bwd(lh, synth.config("tiny", N=1552, L=3, p=4, k=40, H=1), heads=[0], grad_dtype="bf16")
+
+
+def test_backward_properties_scale_and_determinism(lh):
+    import torch
+    cfg = synth.config("bwd8k", N=65536, H=2)
+    inp = synth.make_inputs(cfg, with_do=True)
+    run = run_forward(lh, cfg, inp)
+    dout = to_dev(inp["do"], cfg["dtype"])
+    g1 = lh.backward(run["q"], run["k"], run["v"], dout, run["saved"], run["plan"], grad_dtype=torch.float32)
+    g2 = lh.backward(run["q"], run["k"], run["v"], dout * 2, run["saved"], run["plan"], grad_dtype=torch.float32)
+    g3 = lh.backward(run["q"], run["k"], run["v"], dout, run["saved"], run["plan"], grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, c)
+        assert torch.equal(2 * a, b)

@@ -440,3 +440,14 @@ def test_backward_L1_textbook():
             ek[j] += dz * s * q[i]
     for a, b in ((dq, eq), (dk, ek), (dv, ev)):
         assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_attend_rows_matches_attend():
+    rng = np.random.default_rng(15)
+    S, d = 300, 8
+    qt, kt, vt = rng.standard_normal((3, S, d))
+    o, lse = orc.attend(qt, kt, vt, row_block=64)
+    rows = [0, 1, 63, 64, 150, 299]
+    o2, lse2 = orc.attend_rows(qt, kt, vt, rows)
+    assert np.max(np.abs(o2 - o[rows])) < 1e-13
+    assert np.max(np.abs(lse2 - lse[rows])) < 1e-13
