@@ -158,7 +158,7 @@ def main() -> int:
     # stream it runs on
     qt = lh.saved_view(saved, plan, "qt")
     kt = lh.saved_view(saved, plan, "kt")
-    vop = lh.saved_view(saved, plan, "vt")
+    vop = lh.saved_view(saved, plan, "vtt" if io == torch.bfloat16 else "vt")
     ot = torch.empty((BH, S, d), dtype=torch.float32, device=dev)
     lse = torch.empty((BH, S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -178,7 +178,7 @@ def main() -> int:
     extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "attn_fwd_kernel_ms": attn_ms,
              "attn_fwd_flops": flops, "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
     if args.dense:
-        vt_dense = v.reshape(BH, N, d)
+        vt_dense = v.reshape(BH, N, d).transpose(1, 2).contiguous() if io == torch.bfloat16 else v.reshape(BH, N, d)
         od = torch.empty((BH, N, d), dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
       for (int idx = tid; idx < D * 64; idx += kThreads) {
         const int dd = idx / 64;
         const int c = idx % 64;
-        if (c < nb) vtt[((long long)h * D + dd) * s.S + m0 + b0 + c] = vstage[c][dd];
+        if (c < nb) vtt[((long long)h * D + dd) * s.Sv + m0 + b0 + c] = vstage[c][dd];
       }
       __syncthreads();
     }

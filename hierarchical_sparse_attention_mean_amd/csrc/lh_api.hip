@@ -13,6 +13,8 @@
 namespace lh {
 hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st);
+hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int vstride, const void *qt, const void *kt, const void *vtt,
+                                float *ot, float *lse, hipStream_t st);
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, hipStream_t st);
@@ -84,6 +86,7 @@ lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
   }
   s->Bsel = (int)budget;
   s->S = s->n[L - 1] + s->Bsel;
+  s->Sv = (s->S + 7) & ~7;
   if ((int64_t)s->S * d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
   s->ntile = (s->N + lh::kCompactTile - 1) / lh::kCompactTile;
   return LH_OK;
@@ -105,7 +108,7 @@ void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
   o->qt = take(es * BH * S * d);
   o->kt = take(es * BH * S * d);
   o->vt = take(es * BH * S * d);
-  o->vtt = take(es * BH * S * d);
+  o->vtt = take(es * BH * (size_t)s.Sv * d);
   o->ot = take(4 * BH * S * d);
   o->lse = take(4 * BH * S);
   o->total = cur;
@@ -113,6 +116,7 @@ void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
   o->E = s.E;
   o->Bsel = s.Bsel;
   o->S = s.S;
+  o->Sv = s.Sv;
 }
 
 void fwd_ws_layout(const lh::Shape &s, lh::FwdWs *w) {
@@ -243,7 +247,10 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
     return st;
   // (iii) causal attention over the sub-sequence
   hipError_t e;
-  e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
+  if (s.io == LH_BF16)
+    e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
+  else
+    e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
   if ((st = hip_check(e, "attention")) != LH_OK) return st;
   // (iv) scatter-back
   if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
@@ -308,7 +315,8 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *vt, flo
   if (lse && ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be 4-byte aligned");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, q, k, vt, o, lse, hs);
+  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)((S + 7) & ~7), q, k, vt, o, lse, hs);
+  else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, q, k, vt, o, lse, hs);
   return hip_check(e, "attention");
 }
 

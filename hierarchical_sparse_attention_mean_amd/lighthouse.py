@@ -39,7 +39,7 @@ class LighthouseError(RuntimeError):
 class SavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "ot", "lse", "total")] + \
-               [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S")]
+               [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S", "Sv")]
 
 
 _i, _i64, _sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -214,7 +214,7 @@ def saved_view(saved, plan, name):
     spec = {
         "scores": (torch.float32, (BH, 2, P)), "flags": (torch.uint8, (BH, P)), "slot": (torch.int32, (BH, P)),
         "coords": (torch.int32, (BH, S)), "qt": (io, (BH, S, d)), "kt": (io, (BH, S, d)), "vt": (io, (BH, S, d)),
-        "vtt": (io, (BH, d, S)), "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
+        "vtt": (io, (BH, d, lay["Sv"])), "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
     }[name]
     dt, shape = spec
     n = 1

@@ -69,7 +69,8 @@ typedef struct lh_saved_layout_t {
   size_t qt;       /* io    [BH][S][d]  gathered Q~ (topological order) */
   size_t kt;       /* io    [BH][S][d]  gathered K~ */
   size_t vt;       /* io    [BH][S][d]  gathered V~ */
-  size_t vtt;      /* io    [BH][d][S]  V~ transposed (operand layout of the MFMA P.V product) */
+  size_t vtt;      /* io    [BH][d][Sv] V~ transposed, row stride Sv = S rounded up to a multiple
+                            of 8 (operand layout of the bf16 MFMA P.V product; LH_BF16 only) */
   size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
   size_t lse;      /* fp32  [BH][S]     natural-log log-sum-exp of each O~ row's logits */
   size_t total;    /* bytes needed */
@@ -77,6 +78,7 @@ typedef struct lh_saved_layout_t {
   int64_t E;       /* candidate (non-coarsest) entries per head */
   int64_t Bsel;    /* selected candidates per head */
   int64_t S;       /* gathered length per head */
+  int64_t Sv;      /* row stride of vtt: S rounded up to a multiple of 8 */
 } lh_saved_layout_t;
 
 /* Host-only.  Validates the shape and returns S and the byte sizes the caller
@@ -117,8 +119,10 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
 /* Dense causal softmax attention, softmax(Q K^T / sqrt(d) + causal) V, on given
  * [BH,S,d] tensors (Sec. 3.1, Eq. 1): the kernel of stage (iii), exposed for the
  * dense baseline at S = N.
- *   q, k   : [BH][S][d] dtype `io`;  vt: V transposed [BH][d][S] for LH_BF16,
- *            V itself [BH][S][d] for LH_F32.
+ *   q, k   : [BH][S][d] dtype `io`.
+ *   vt     : LH_BF16: V transposed, [BH][d][Sv] with row stride Sv = S rounded up
+ *            to a multiple of 8 (the bf16 MFMA kernel's operand layout);
+ *            LH_F32: V itself, [BH][S][d].
  *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
 lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,
                                int BH, int64_t S, int d, lh_dtype io, void *stream);

@@ -3,8 +3,10 @@
 Two references, both the fp64 oracle with the GPU's selection injected:
   * stage-consistent: the oracle's adjoints (scatter, attention, gather, pool)
     evaluated on the GPU's own gathered rows, so only the kernels' arithmetic
-    differs -- bar 1e-3 of the gradient's largest magnitude (fp32 accumulation
-    over <= S terms, bf16 operands read exactly);
+    differs -- bar (relative to the gradient's largest magnitude) 1e-5 in fp32
+    mode (fp32 accumulation over <= S terms) and 2^-8 in bf16 mode, where the
+    backward consumes the forward's O~ and LSE, whose P.V product took the
+    probabilities rounded to bf16 (one bf16 rounding, 2^-9 relative, per weight);
   * end to end: the oracle's own fp64 pyramid and backward -- bar 2e-2 of the
     gradient's largest magnitude, the forward's bf16 bar applied to the
     gradients' scale (pooled rows are stored in bf16, so the logits of pooled
@@ -21,7 +23,7 @@ from hierarchical_sparse_attention_mean_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-STAGE_TOL = 1e-3
+STAGE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8}
 E2E_TOL = 2e-2
 
 
@@ -65,7 +67,7 @@ def _run_bwd(lh, cfg, heads, grad_dtype="f32"):
             ee = np.max(np.abs(a - re)) / scale
             say(f"  head {h} {name}: max|g|={scale:.3e} stage err={es:.3e} end-to-end err={ee:.3e}")
             extra = 2.0 ** -8 if grad_dtype == "bf16" else 0.0
-            assert es <= STAGE_TOL + extra
+            assert es <= STAGE_TOL[cfg["dtype"]] + extra
             assert ee <= E2E_TOL + extra
     return run, dq, dk, dv
 
