@@ -93,19 +93,6 @@ __global__ __launch_bounds__(256) void k_attn_fwd_valu(int S, const T *__restric
   if (part == 0 && lse) lse[hb + qi] = (m + log2f(l)) * kLn2;
 }
 
-// delta_m = sum_d dO~[m][d] * O~[m][d]
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_delta(long long rows, const float *__restrict__ ot,
-                                                    const float *__restrict__ dot, float *__restrict__ delta) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float acc = 0.f;
-  for (int c = lane; c < D; c += 64) acc = fmaf(ot[row * D + c], dot[row * D + c], acc);
-  for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-  if (lane == 0) delta[row] = acc;
-}
-
 // dQ~ (query-stationary): dq_m = scale * sum_{m' <= m} P_mm' (dP_mm' - delta_m) K_m'
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_attn_dq_valu(int S, const T *__restrict__ qt, const T *__restrict__ kt,
@@ -252,9 +239,7 @@ hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, co
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, hipStream_t st) {
-  const long long rows = (long long)BH * S;
-  if (d == 128) k_attn_delta<128><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(rows, ot, dot, delta);
-  else k_attn_delta<64><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(rows, ot, dot, delta);
+  (void)ot;   // delta = rowsum(dO~ * O~) comes from the scatter adjoint
   dim3 grid((S + BM - 1) / BM, BH);
 #define LH_BWD(T, D)                                                                                            \
   do {                                                                                                          \

@@ -64,11 +64,13 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
                                                             const int *__restrict__ tilecount, int *__restrict__ slot,
                                                             int *__restrict__ coords, T *__restrict__ qt,
                                                             T *__restrict__ kt, T *__restrict__ vt,
-                                                            T *__restrict__ vtt) {
+                                                            T *__restrict__ vtt, T *__restrict__ qtt,
+                                                            T *__restrict__ ktt) {
   __shared__ int red[kThreads / 64];
   __shared__ int scan[kThreads];
   __shared__ int lflat[kCompactTile * 2];     // flat indices of this tile's slots (spills to global if more)
-  __shared__ T vstage[64][D + 2];
+  // bf16 only: rows of the current batch of 64 slots, for the transposed copies
+  __shared__ T stage[3][sizeof(T) == 2 ? 64 : 1][D + 2];
   const int h = blockIdx.y;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
@@ -159,9 +161,15 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
         *reinterpret_cast<uint4 *>(qt + dst) = a;
         *reinterpret_cast<uint4 *>(kt + dst) = b;
         *reinterpret_cast<uint4 *>(vt + dst) = c;
+        const T *ca = reinterpret_cast<const T *>(&a);
+        const T *cb = reinterpret_cast<const T *>(&b);
         const T *cv = reinterpret_cast<const T *>(&c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vstage[r][j * 8 + e] = cv[e];
+        for (int e = 0; e < 8; ++e) {
+          stage[0][r][j * 8 + e] = ca[e];
+          stage[1][r][j * 8 + e] = cb[e];
+          stage[2][r][j * 8 + e] = cv[e];
+        }
       } else {
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
@@ -175,13 +183,18 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
       }
     }
     if constexpr (sizeof(T) == 2) {
-      // V~ transposed: row dd of V~^T holds column dd of V~, for this batch of slots
+      // transposed copies: row dd of X~^T holds column dd of X~, for this batch of slots
       __syncthreads();
       const int nb = min(64, ntot - b0);
       for (int idx = tid; idx < D * 64; idx += kThreads) {
         const int dd = idx / 64;
         const int c = idx % 64;
-        if (c < nb) vtt[((long long)h * D + dd) * s.Sv + m0 + b0 + c] = vstage[c][dd];
+        if (c < nb) {
+          const long long o = ((long long)h * D + dd) * s.Sv + m0 + b0 + c;
+          qtt[o] = stage[0][c][dd];
+          ktt[o] = stage[1][c][dd];
+          vtt[o] = stage[2][c][dd];
+        }
       }
       __syncthreads();
     }
@@ -192,14 +205,15 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
 
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                                  const FwdWs &w, const uint8_t *flags, int *slot, int *coords, void *qt,
-                                 void *kt, void *vt, void *vtt, hipStream_t st) {
+                                 void *kt, void *vt, void *vtt, void *qtt, void *ktt, hipStream_t st) {
   char *wsb = reinterpret_cast<char *>(ws);
   int *tc = reinterpret_cast<int *>(wsb + w.tilecount);
   dim3 grid(s.ntile, s.BH);
   k_compact_count<<<grid, kThreads, 0, st>>>(s, flags, tc);
 #define LH_GATHER(T, D)                                                                                         \
   k_compact_gather<T, D><<<grid, kThreads, 0, st>>>(s, (const T *)q, (const T *)k, (const T *)v, wsb, w, flags, \
-                                                    tc, slot, coords, (T *)qt, (T *)kt, (T *)vt, (T *)vtt)
+                                                    tc, slot, coords, (T *)qt, (T *)kt, (T *)vt, (T *)vtt, \
+                                                    (T *)qtt, (T *)ktt)
   if (s.io == LH_BF16) {
     if (s.d == 128) LH_GATHER(uint16_t, 128);
     else LH_GATHER(uint16_t, 64);

@@ -77,30 +77,96 @@ __device__ __forceinline__ float4 ld4(const void *p, long long off, int dtype) {
   return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + off);
 }
 
-template <int D>
+// One work-group per 64 consecutive slots; 4 lanes per slot, each summing D/4
+// columns of dO over the entry's scatter range (t ascending), then
+//   delta_m = sum_d dO~[m][d] * O~[m][d]   (the softmax-backward row term)
+// with dO~ as the attention backward will read it (bf16-rounded in bf16 mode).
+// fp32 mode writes dO~ in fp32; bf16 mode writes dO~ in bf16, row-major and
+// transposed ([d][Sv], through an LDS stage so the columns are written
+// coalesced).
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__restrict__ dout, int dout_dtype,
-                                                     const int *__restrict__ coords, float *__restrict__ dot) {
-  constexpr int C4 = D / 4;
+                                                     const int *__restrict__ coords, const float *__restrict__ ot,
+                                                     float *__restrict__ dot32, uint16_t *__restrict__ dotb,
+                                                     uint16_t *__restrict__ dott, float *__restrict__ delta) {
+  constexpr int DP = D / 4;
+  __shared__ uint16_t stage[BF16 ? 64 : 1][D + 2];
   const int h = blockIdx.y;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)s.S * C4) return;
-  const int m = (int)(idx / C4);
-  const int c = (int)(idx % C4);
-  const int f = coords[(long long)h * s.S + m];
-  int l = 0;
-  while (l + 1 < s.L && f >= s.off[l + 1]) ++l;
-  const int i = f - s.off[l];
-  const int lo = (i + 1) * s.pw[l] - 1;
-  const int hi = min(s.N - 1, lo + s.pw[l] - 1);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int t = lo; t <= hi; ++t) {
-    const float4 x = ld4(dout, ((long long)h * s.N + t) * D + c * 4, dout_dtype);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
+  const int m0 = blockIdx.x * 64;
+  const int r = threadIdx.x >> 2;
+  const int part = threadIdx.x & 3;
+  const int m = m0 + r;
+  const bool active = m < s.S;
+  float acc[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) acc[e] = 0.f;
+  if (active) {
+    const int f = coords[(long long)h * s.S + m];
+    int l = 0;
+    while (l + 1 < s.L && f >= s.off[l + 1]) ++l;
+    const int i = f - s.off[l];
+    const int lo = (i + 1) * s.pw[l] - 1;
+    const int hi = min(s.N - 1, lo + s.pw[l] - 1);
+    for (int t = lo; t <= hi; ++t) {
+      const long long base = ((long long)h * s.N + t) * D + part * DP;
+#pragma unroll
+      for (int e = 0; e < DP; e += 4) {
+        const float4 x = ld4(dout, base + e, dout_dtype);
+        acc[e] += x.x;
+        acc[e + 1] += x.y;
+        acc[e + 2] += x.z;
+        acc[e + 3] += x.w;
+      }
+    }
   }
-  reinterpret_cast<float4 *>(dot + ((long long)h * s.S + m) * D)[c] = acc;
+  const long long row = ((long long)h * s.S + m) * D + part * DP;
+  float dl = 0.f;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < DP; ++e) {
+      const uint16_t b = f32_to_bf16_rne(acc[e]);
+      acc[e] = bf16_to_f32(b);
+      stage[r][part * DP + e] = b;
+    }
+  }
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < DP; e += 4) {
+      const float4 o4 = *reinterpret_cast<const float4 *>(ot + row + e);
+      dl = fmaf(acc[e], o4.x, dl);
+      dl = fmaf(acc[e + 1], o4.y, dl);
+      dl = fmaf(acc[e + 2], o4.z, dl);
+      dl = fmaf(acc[e + 3], o4.w, dl);
+    }
+  }
+  dl += __shfl_xor(dl, 1);
+  dl += __shfl_xor(dl, 2);
+  if (active) {
+    if (part == 0) delta[(long long)h * s.S + m] = dl;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < DP; e += 8) {
+        uint4 w;
+        w.x = (unsigned)stage[r][part * DP + e] | ((unsigned)stage[r][part * DP + e + 1] << 16);
+        w.y = (unsigned)stage[r][part * DP + e + 2] | ((unsigned)stage[r][part * DP + e + 3] << 16);
+        w.z = (unsigned)stage[r][part * DP + e + 4] | ((unsigned)stage[r][part * DP + e + 5] << 16);
+        w.w = (unsigned)stage[r][part * DP + e + 6] | ((unsigned)stage[r][part * DP + e + 7] << 16);
+        *reinterpret_cast<uint4 *>(dotb + row + e) = w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DP; e += 4)
+        *reinterpret_cast<float4 *>(dot32 + row + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+  }
+  if constexpr (BF16) {
+    __syncthreads();
+    const int nb = min(64, s.S - m0);
+    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
+      const int dd = idx / 64, c = idx % 64;
+      if (c < nb) dott[((long long)h * D + dd) * s.Sv + m0 + c] = stage[c][dd];
+    }
+  }
 }
 
 template <int D>
@@ -156,13 +222,19 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *slot, const int *coords,
-                              float *dot, hipStream_t st) {
-  (void)slot;
-  const long long n = (long long)s.S * (s.d / 4);
-  dim3 grid((unsigned)((n + 255) / 256), s.BH);
-  if (s.d == 128) k_scatter_bwd<128><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, dot);
-  else k_scatter_bwd<64><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, dot);
+hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
+                              float *dot32, uint16_t *dotb, uint16_t *dott, float *delta, hipStream_t st) {
+  dim3 grid((unsigned)((s.S + 63) / 64), s.BH);
+  const bool bf = s.io == LH_BF16;
+#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, dott, delta)
+  if (s.d == 128) {
+    if (bf) LH_SB(128, true);
+    else LH_SB(128, false);
+  } else {
+    if (bf) LH_SB(64, true);
+    else LH_SB(64, false);
+  }
+#undef LH_SB
   return hipGetLastError();
 }
 

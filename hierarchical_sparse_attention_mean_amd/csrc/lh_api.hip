@@ -18,6 +18,10 @@ hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int vstride, const void *q
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, hipStream_t st);
+hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
+                                const void *qtt, const void *ktt, const void *dotb, const void *dott,
+                                const float *lse, const float *delta, float *dqt, float *dkt, float *dvt,
+                                hipStream_t st);
 }  // namespace lh
 
 namespace {
@@ -109,6 +113,8 @@ void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
   o->kt = take(es * BH * S * d);
   o->vt = take(es * BH * S * d);
   o->vtt = take(es * BH * (size_t)s.Sv * d);
+  o->qtt = take(es * BH * (size_t)s.Sv * d);
+  o->ktt = take(es * BH * (size_t)s.Sv * d);
   o->ot = take(4 * BH * S * d);
   o->lse = take(4 * BH * S);
   o->total = cur;
@@ -148,7 +154,10 @@ void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
     cur = align_up(cur + bytes);
     return at;
   };
-  w->dot = take(4 * BH * S * d);
+  const bool bf = s.io == LH_BF16;
+  w->dot = take(bf ? 0 : 4 * BH * S * d);
+  w->dotb = take(bf ? 2 * BH * S * d : 0);
+  w->dott = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
   w->delta = take(4 * BH * S);
   w->dqt = take(4 * BH * S * d);
   w->dkt = take(4 * BH * S * d);
@@ -242,7 +251,7 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   if ((st = hip_check(lh::launch_topk(s, ws, fw, flags, hs), "topk")) != LH_OK) return st;
   // (iii) topological compaction + gather
   if ((st = hip_check(lh::launch_compact_gather(s, q, k, v, ws, fw, flags, slot, coords, sv + sl.qt, sv + sl.kt,
-                                                sv + sl.vt, sv + sl.vtt, hs),
+                                                sv + sl.vt, sv + sl.vtt, sv + sl.qtt, sv + sl.ktt, hs),
                       "compact_gather")) != LH_OK)
     return st;
   // (iii) causal attention over the sub-sequence
@@ -286,6 +295,8 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   const float *ot = reinterpret_cast<const float *>(sv + sl.ot);
   const float *lse = reinterpret_cast<const float *>(sv + sl.lse);
   float *dot = reinterpret_cast<float *>(wb + bw.dot);
+  uint16_t *dotb = reinterpret_cast<uint16_t *>(wb + bw.dotb);
+  uint16_t *dott = reinterpret_cast<uint16_t *>(wb + bw.dott);
   float *delta = reinterpret_cast<float *>(wb + bw.delta);
   float *dqt = reinterpret_cast<float *>(wb + bw.dqt);
   float *dkt = reinterpret_cast<float *>(wb + bw.dkt);
@@ -293,12 +304,21 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   (void)q;
   (void)k;
   (void)v;
-  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, slot, coords, dot, hs), "scatter_bwd")) != LH_OK)
+  (void)slot;
+  // adjoint of the scatter: dO~ (and delta = rowsum(dO~ * O~))
+  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, dot, dotb, dott, delta, hs),
+                      "scatter_bwd")) != LH_OK)
     return st;
+  // adjoint of the sub-sequence attention
   hipError_t e;
-  e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
-                               dkt, dvt, hs);
+  if (s.io == LH_BF16)
+    e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
+                                 dotb, dott, lse, delta, dqt, dkt, dvt, hs);
+  else
+    e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
+                                 dkt, dvt, hs);
   if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  // adjoint of the gather and of the pooling
   if ((st = hip_check(lh::launch_pool_bwd(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype, hs), "pool_bwd")) != LH_OK)
     return st;
   return LH_OK;

@@ -59,7 +59,9 @@ struct FwdWs {
 
 // Backward workspace layout.
 struct BwdWs {
-  size_t dot;     // fp32 [BH][S][d]  gradient of O~
+  size_t dot;     // fp32 [BH][S][d]  gradient of O~ (LH_F32 mode)
+  size_t dotb;    // bf16 [BH][S][d]  gradient of O~ (LH_BF16 mode)
+  size_t dott;    // bf16 [BH][d][Sv] gradient of O~, transposed (LH_BF16 mode)
   size_t delta;   // fp32 [BH][S]     rowsum(dO~ * O~)
   size_t dqt;     // fp32 [BH][S][d]
   size_t dkt;     // fp32 [BH][S][d]
@@ -95,11 +97,11 @@ hipError_t launch_topk_init(const Shape &s, void *ws, const FwdWs &w, hipStream_
 hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, uint8_t *flags, hipStream_t st);
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                                  const FwdWs &w, const uint8_t *flags, int *slot, int *coords,
-                                 void *qt, void *kt, void *vt, void *vtt, hipStream_t st);
+                                 void *qt, void *kt, void *vt, void *vtt, void *qtt, void *ktt, hipStream_t st);
 hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void *o, int o_dtype,
                           hipStream_t st);
-hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *slot,
-                              const int *coords, float *dot, hipStream_t st);
+hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
+                              float *dot32, uint16_t *dotb, uint16_t *dott, float *delta, hipStream_t st);
 hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, const float *dkt,
                            const float *dvt, void *dq, void *dk, void *dv, int grad_dtype, hipStream_t st);
 

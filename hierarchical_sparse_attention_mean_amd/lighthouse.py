@@ -38,7 +38,8 @@ class LighthouseError(RuntimeError):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "ot", "lse", "total")] + \
+                ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse",
+                          "total")] + \
                [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S", "Sv")]
 
 
@@ -214,7 +215,8 @@ def saved_view(saved, plan, name):
     spec = {
         "scores": (torch.float32, (BH, 2, P)), "flags": (torch.uint8, (BH, P)), "slot": (torch.int32, (BH, P)),
         "coords": (torch.int32, (BH, S)), "qt": (io, (BH, S, d)), "kt": (io, (BH, S, d)), "vt": (io, (BH, S, d)),
-        "vtt": (io, (BH, d, lay["Sv"])), "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
+        "vtt": (io, (BH, d, lay["Sv"])), "qtt": (io, (BH, d, lay["Sv"])), "ktt": (io, (BH, d, lay["Sv"])),
+        "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
     }[name]
     dt, shape = spec
     n = 1

@@ -71,6 +71,8 @@ typedef struct lh_saved_layout_t {
   size_t vt;       /* io    [BH][S][d]  gathered V~ */
   size_t vtt;      /* io    [BH][d][Sv] V~ transposed, row stride Sv = S rounded up to a multiple
                             of 8 (operand layout of the bf16 MFMA P.V product; LH_BF16 only) */
+  size_t qtt;      /* io    [BH][d][Sv] Q~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
+  size_t ktt;      /* io    [BH][d][Sv] K~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
   size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
   size_t lse;      /* fp32  [BH][S]     natural-log log-sum-exp of each O~ row's logits */
   size_t total;    /* bytes needed */

@@ -56,7 +56,7 @@ def gpu_head(lh, run: dict, h: int) -> dict:
     out["flags"] = lh.saved_view(saved, plan, "flags")[h].cpu().numpy().astype(bool)
     out["slot"] = lh.saved_view(saved, plan, "slot")[h].cpu().numpy()
     out["coords"] = lh.saved_view(saved, plan, "coords")[h].cpu().numpy().astype(np.int64)
-    for n in ("qt", "kt", "vt", "vtt"):
+    for n in ("qt", "kt", "vt", "vtt", "qtt", "ktt"):
         out[n] = bf16_tensor_to_f64(lh.saved_view(saved, plan, n)[h])
     out["ot32"] = lh.saved_view(saved, plan, "ot")[h].cpu().numpy()
     out["lse"] = lh.saved_view(saved, plan, "lse")[h].cpu().numpy().astype(np.float64)

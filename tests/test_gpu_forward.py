@@ -63,7 +63,8 @@ def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True,
         rel = 2.0 ** -8 if dt == "bf16" else 2e-6
         assert np.all(np.abs(got[~base] - ref[~base]) <= rel * np.abs(ref[~base]) + 1e-6), f"{name} pooled rows"
     if dt == "bf16":
-        assert np.array_equal(g["vtt"][:, :S].T, g["vt"]), "V~ transposed copy differs"
+        for tn, n in (("vtt", "vt"), ("qtt", "qt"), ("ktt", "kt")):
+            assert np.array_equal(g[tn][:, :S].T, g[n]), f"{tn}: transposed copy differs"
     # ---- attention on the GPU's own gathered rows
     if full_attention:
         ot_ref, lse_ref = orc.attend(g["qt"], g["kt"], g["vt"])
@@ -173,7 +174,7 @@ def test_deterministic(lh):
     a = run_forward(lh, cfg, inp, out_dtype="bf16")
     b = run_forward(lh, cfg, inp, out_dtype="bf16")
     assert torch.equal(a["o"].view(torch.int16), b["o"].view(torch.int16))
-    for n in ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "ot", "lse"):
+    for n in ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse"):
         x = lh.saved_view(a["saved"], a["plan"], n)
         y = lh.saved_view(b["saved"], b["plan"], n)
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
