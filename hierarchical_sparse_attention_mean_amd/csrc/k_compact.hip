@@ -199,6 +199,18 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
       __syncthreads();
     }
   }
+  if constexpr (sizeof(T) == 2) {
+    // zero the padding columns S..Sv-1 of the transposed copies (read as masked keys)
+    if (tile == s.ntile - 1) {
+      const int pad = s.Sv - s.S;
+      for (int idx = tid; idx < D * pad; idx += kThreads) {
+        const long long o = ((long long)h * D + idx / pad) * s.Sv + s.S + idx % pad;
+        qtt[o] = 0;
+        ktt[o] = 0;
+        vtt[o] = 0;
+      }
+    }
+  }
 }
 
 }  // namespace

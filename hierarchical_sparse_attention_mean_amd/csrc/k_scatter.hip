@@ -161,10 +161,11 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   }
   if constexpr (BF16) {
     __syncthreads();
+    // columns past S (up to the padded stride Sv) are written as zeros
     const int nb = min(64, s.S - m0);
     for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
       const int dd = idx / 64, c = idx % 64;
-      if (c < nb) dott[((long long)h * D + dd) * s.Sv + m0 + c] = stage[c][dd];
+      if (m0 + c < s.Sv) dott[((long long)h * D + dd) * s.Sv + m0 + c] = c < nb ? stage[c][dd] : (uint16_t)0;
     }
   }
 }

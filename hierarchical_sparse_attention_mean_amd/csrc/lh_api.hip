@@ -90,7 +90,7 @@ lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
   }
   s->Bsel = (int)budget;
   s->S = s->n[L - 1] + s->Bsel;
-  s->Sv = (s->S + 7) & ~7;
+  s->Sv = (s->S + 63) & ~63;
   if ((int64_t)s->S * d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
   s->ntile = (s->N + lh::kCompactTile - 1) / lh::kCompactTile;
   return LH_OK;
@@ -335,7 +335,7 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *vt, flo
   if (lse && ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be 4-byte aligned");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)((S + 7) & ~7), q, k, vt, o, lse, hs);
+  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)((S + 63) & ~63), q, k, vt, o, lse, hs);
   else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, q, k, vt, o, lse, hs);
   return hip_check(e, "attention");
 }

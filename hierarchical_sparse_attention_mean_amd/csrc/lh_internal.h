@@ -28,7 +28,7 @@ struct Shape {
   int E;                     // candidates per head (levels 0..L-2)
   int Bsel;                  // selected candidates per head
   int S;                     // gathered length per head
-  int Sv;                    // row stride of V~ transposed: S rounded up to a multiple of 8
+  int Sv;                    // row stride of the transposed copies: S rounded up to a multiple of 64
   int ntile;                 // compaction tiles per head
 };
 

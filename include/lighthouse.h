@@ -70,7 +70,8 @@ typedef struct lh_saved_layout_t {
   size_t kt;       /* io    [BH][S][d]  gathered K~ */
   size_t vt;       /* io    [BH][S][d]  gathered V~ */
   size_t vtt;      /* io    [BH][d][Sv] V~ transposed, row stride Sv = S rounded up to a multiple
-                            of 8 (operand layout of the bf16 MFMA P.V product; LH_BF16 only) */
+                            of 64, columns S..Sv-1 zero (operand layout of the bf16 MFMA P.V
+                            product; LH_BF16 only) */
   size_t qtt;      /* io    [BH][d][Sv] Q~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
   size_t ktt;      /* io    [BH][d][Sv] K~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
   size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
@@ -80,7 +81,7 @@ typedef struct lh_saved_layout_t {
   int64_t E;       /* candidate (non-coarsest) entries per head */
   int64_t Bsel;    /* selected candidates per head */
   int64_t S;       /* gathered length per head */
-  int64_t Sv;      /* row stride of vtt: S rounded up to a multiple of 8 */
+  int64_t Sv;      /* row stride of vtt, qtt, ktt: S rounded up to a multiple of 64 */
 } lh_saved_layout_t;
 
 /* Host-only.  Validates the shape and returns S and the byte sizes the caller
@@ -123,7 +124,8 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
  * dense baseline at S = N.
  *   q, k   : [BH][S][d] dtype `io`.
  *   vt     : LH_BF16: V transposed, [BH][d][Sv] with row stride Sv = S rounded up
- *            to a multiple of 8 (the bf16 MFMA kernel's operand layout);
+ *            to a multiple of 64 and columns S..Sv-1 zero (the bf16 MFMA kernel's
+ *            operand layout);
  *            LH_F32: V itself, [BH][S][d].
  *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
 lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,

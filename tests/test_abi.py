@@ -32,7 +32,7 @@ def test_query_matches_closed_form(lh, B, H, N, d, L, p, k, io):
     st, lay = lh.lh_saved_layout(B, H, N, d, L, p, k, io)
     assert st == 0
     assert lay["S"] == S and lay["P"] == sum(sizes) and lay["E"] == sum(sizes[:-1])
-    assert lay["Sv"] == (S + 7) // 8 * 8
+    assert lay["Sv"] == (S + 63) // 64 * 64
     es = 2 if io == "bf16" else 4
     BH = B * H
     order = ["scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse"]
