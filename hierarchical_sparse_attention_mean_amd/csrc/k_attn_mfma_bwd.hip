@@ -13,12 +13,17 @@
 //                    dO~ as B operands; per key tile it forms S^T = K~ Q~^T and
 //                    dP^T = V~ dO~^T (lane = one query), dS^T in registers, and
 //                    accumulates dQ^T += K~^T dS^T with K~^T from LDS.
+//                    8 wavefronts, 256 queries per work-group.
 //   k_attn_bwd_dkdv  key-stationary: a wavefront holds 32 key rows of K~ and V~
 //                    as B operands; per query tile it forms S = Q~ K~^T and
 //                    dP = dO~ V~^T (lane = one key), and accumulates
 //                    dV^T += dO~^T P and dK^T += Q~^T dS with the transposed
-//                    query-side operands from LDS.
-// The transposed operands (K~^T, Q~^T, dO~^T, row stride Sv) are written by the
+//                    query-side operands from LDS.  4 wavefronts, 128 keys per
+//                    work-group (the accumulators need the register file of a
+//                    whole SIMD).
+// Both stream their tiles through double-buffered LDS with the next tile's
+// global loads in flight in registers.  The transposed operands (K~^T, Q~^T,
+// dO~^T; row stride Sv, a multiple of 64, zero padded) are written by the
 // gather and by the scatter adjoint, so every LDS operand is read as rows.
 #include "lh_internal.h"
 
@@ -41,65 +46,78 @@ __device__ __forceinline__ bf16x8 lds_split8(const uint16_t *p) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// stage rows [r0, r0+R) of a [S][D] bf16 array into LDS with row stride LS
-template <int R, int D, int LS>
-__device__ __forceinline__ void stage_rows(uint16_t *dst, const uint16_t *src, int r0, int S) {
-#pragma unroll
-  for (int it = 0; it < (R * D) / (8 * 256); ++it) {
-    const int idx = it * 256 + threadIdx.x;
-    const int r = idx / (D / 8), cc = idx % (D / 8);
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r0 + r < S) val = *reinterpret_cast<const uint4 *>(src + (long long)(r0 + r) * D + cc * 8);
-    *reinterpret_cast<uint4 *>(&dst[r * LS + cc * 8]) = val;
-  }
+__device__ __forceinline__ void st_split8(uint16_t *p, uint4 v) {
+  uint2 *d2 = reinterpret_cast<uint2 *>(p);
+  d2[0] = make_uint2(v.x, v.y);
+  d2[1] = make_uint2(v.z, v.w);
 }
 
-// stage columns [c0, c0+C) of a transposed [D][Sv] bf16 array into LDS [D][LS]
-template <int C, int D, int LS>
-__device__ __forceinline__ void stage_cols(uint16_t *dst, const uint16_t *src, int c0, int S, int Sv) {
-#pragma unroll
-  for (int it = 0; it < (C * D) / (8 * 256); ++it) {
-    const int idx = it * 256 + threadIdx.x;
-    const int r = idx / (C / 8), cc = idx % (C / 8);
-    const int kk = c0 + cc * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (kk + 8 <= S) {
-      val = *reinterpret_cast<const uint4 *>(src + (long long)r * Sv + kk);
-    } else {
-      uint16_t tmp[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tmp[e] = (kk + e < S) ? src[(long long)r * Sv + kk + e] : (uint16_t)0;
-      val = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16), tmp[4] | (tmp[5] << 16),
-                       tmp[6] | (tmp[7] << 16));
-    }
-    uint2 *d2 = reinterpret_cast<uint2 *>(&dst[r * LS + cc * 8]);
-    d2[0] = make_uint2(val.x, val.y);
-    d2[1] = make_uint2(val.z, val.w);
-  }
-}
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqBM = 32 * kDqWaves;
+constexpr int kDqBN = 64;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(int S, int Sv, int BH, const uint16_t *__restrict__ qt,
-                                                        const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
-                                                        const uint16_t *__restrict__ ktt,
-                                                        const uint16_t *__restrict__ dotb,
-                                                        const float *__restrict__ lse, const float *__restrict__ delta,
-                                                        float *__restrict__ dqt) {
-  constexpr int BM = 128, BN = 64;
+struct DqTile {
+  static constexpr int KS = D + 8;
+  static constexpr int TS = kDqBN + 4;
+  static constexpr int RCH = kDqBN * D / 8;          // 16-byte chunks of one row tile
+  static constexpr int RPT = RCH / kDqThreads;       // per thread
+  uint16_t k[kDqBN * KS];
+  uint16_t v[kDqBN * KS];
+  uint16_t kt[D * TS];
+};
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, int BH, const uint16_t *__restrict__ qt,
+                                                               const uint16_t *__restrict__ kt,
+                                                               const uint16_t *__restrict__ vt,
+                                                               const uint16_t *__restrict__ ktt,
+                                                               const uint16_t *__restrict__ dotb,
+                                                               const float *__restrict__ lse,
+                                                               const float *__restrict__ delta,
+                                                               float *__restrict__ dqt) {
+  using Tile = DqTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  constexpr int KS = D + 8, TS = BN + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t kts[D * TS];
-  const int nqb = (S + BM - 1) / BM;
+  __shared__ __attribute__((aligned(16))) Tile buf[2];
+  const int nqb = (S + kDqBM - 1) / kDqBM;
   const int h = blockIdx.x % BH;
   const int qb = nqb - 1 - blockIdx.x / BH;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
-  const int q0 = qb * BM, qw = q0 + 32 * w, qi = qw + ln;
+  const int q0 = qb * kDqBM, qw = q0 + 32 * w, qi = qw + ln;
   const long long hbS = (long long)h * S;
   const uint16_t *kh = kt + hbS * D;
   const uint16_t *vh = vt + hbS * D;
   const uint16_t *kth = ktt + (long long)h * D * Sv;
+
+  uint4 rk[Tile::RPT], rv[Tile::RPT], rt[Tile::RPT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < Tile::RPT; ++it) {
+      const int idx = it * kDqThreads + tid;
+      const int r = idx / (D / 8), cc = idx % (D / 8);
+      const bool ok = k0 + r < S;
+      rk[it] = ok ? *reinterpret_cast<const uint4 *>(kh + (long long)(k0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+      rv[it] = ok ? *reinterpret_cast<const uint4 *>(vh + (long long)(k0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+      const int tr = idx / (kDqBN / 8), tc = idx % (kDqBN / 8);
+      rt[it] = *reinterpret_cast<const uint4 *>(kth + (long long)tr * Sv + k0 + tc * 8);
+    }
+  };
+  auto store_tile = [&](Tile &t) {
+#pragma unroll
+    for (int it = 0; it < Tile::RPT; ++it) {
+      const int idx = it * kDqThreads + tid;
+      const int r = idx / (D / 8), cc = idx % (D / 8);
+      *reinterpret_cast<uint4 *>(&t.k[r * Tile::KS + cc * 8]) = rk[it];
+      *reinterpret_cast<uint4 *>(&t.v[r * Tile::KS + cc * 8]) = rv[it];
+      const int tr = idx / (kDqBN / 8), tc = idx % (kDqBN / 8);
+      st_split8(&t.kt[tr * Tile::TS + tc * 8], rt[it]);
+    }
+  };
+
   bf16x8 qf[KC], gf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
@@ -117,43 +135,51 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(int S, int Sv, int BH, c
   f32x16 acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
-  const int kend = min(S, q0 + BM);
-  for (int k0 = 0; k0 < kend; k0 += BN) {
-    __syncthreads();
-    stage_rows<BN, D, KS>(ks, kh, k0, S);
-    stage_rows<BN, D, KS>(vs, vh, k0, S);
-    stage_cols<BN, D, TS>(kts, kth, k0, S, Sv);
-    __syncthreads();
-    if (k0 > qw + 31) continue;
-    f32x16 st[2], dp[2];
+
+  const int kend = min(S, q0 + kDqBM);
+  const int nt = (kend + kDqBN - 1) / kDqBN;
+  load_tile(0);
+  store_tile(buf[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    const int k0 = t * kDqBN;
+    if (t + 1 < nt) load_tile(k0 + kDqBN);
+    const Tile &cur = buf[t & 1];
+    if (k0 <= qw + 31) {
+      f32x16 st[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = (f32x16){};
-      dp[kb] = (f32x16){};
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = (f32x16){};
+        dp[kb] = (f32x16){};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&ks[(32 * kb + ln) * KS + 16 * c + 8 * hf]), qf[c],
-                                                         st[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&vs[(32 * kb + ln) * KS + 16 * c + 8 * hf]), gf[c],
-                                                         dp[kb], 0, 0, 0);
+        for (int c = 0; c < KC; ++c) {
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.k[(32 * kb + ln) * Tile::KS + 16 * c + 8 * hf]),
+                                                           qf[c], st[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.v[(32 * kb + ln) * Tile::KS + 16 * c + 8 * hf]),
+                                                           gf[c], dp[kb], 0, 0, 0);
+        }
       }
+      const bool diag = k0 + kDqBN - 1 > qw;
+      bf16x8 dsf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kb = c >> 1, i = 8 * (c & 1) + j;
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          float pj = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c2, -lse2));
+          if (diag && key > qi) pj = 0.f;
+          dsf[c][j] = (__bf16)(pj * (dp[kb][i] - dl));
+        }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_split8(&cur.kt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), dsf[c], acc[b], 0, 0, 0);
     }
-    bf16x8 dsf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kb = c >> 1, i = 8 * (c & 1) + j;
-        const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const float pj = (key <= qi) ? exp2f(fmaf(st[kb][i], c2, -lse2)) : 0.f;
-        dsf[c][j] = (__bf16)(pj * (dp[kb][i] - dl));
-      }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_split8(&kts[(32 * b + ln) * TS + 16 * c + 4 * hf]), dsf[c],
-                                                         acc[b], 0, 0, 0);
+    if (t + 1 < nt) store_tile(buf[(t + 1) & 1]);
+    __syncthreads();
   }
   if (qi >= S) return;
   const float scale = 1.f / sqrtf((float)D);
@@ -168,33 +194,86 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(int S, int Sv, int BH, c
     }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvBK = 32 * kKvWaves;
+constexpr int kKvBQ = 32;
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(int S, int Sv, int BH, const uint16_t *__restrict__ qt,
-                                                          const uint16_t *__restrict__ kt,
-                                                          const uint16_t *__restrict__ vt,
-                                                          const uint16_t *__restrict__ qtt,
-                                                          const uint16_t *__restrict__ dotb,
-                                                          const uint16_t *__restrict__ dott,
-                                                          const float *__restrict__ lse,
-                                                          const float *__restrict__ delta, float *__restrict__ dkt,
-                                                          float *__restrict__ dvt) {
-  constexpr int BK = 128, BQ = 32;
+struct DkvTile {
+  static constexpr int QS = D + 8;
+  static constexpr int TS = kKvBQ + 4;
+  static constexpr int RCH = kKvBQ * D / 8;
+  static constexpr int RPT = RCH / kKvThreads;
+  uint16_t q[kKvBQ * QS];
+  uint16_t g[kKvBQ * QS];
+  uint16_t qt[D * TS];
+  uint16_t gt[D * TS];
+  float ls[kKvBQ];
+  float dl[kKvBQ];
+};
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, int BH,
+                                                                 const uint16_t *__restrict__ qt,
+                                                                 const uint16_t *__restrict__ kt,
+                                                                 const uint16_t *__restrict__ vt,
+                                                                 const uint16_t *__restrict__ qtt,
+                                                                 const uint16_t *__restrict__ dotb,
+                                                                 const uint16_t *__restrict__ dott,
+                                                                 const float *__restrict__ lse,
+                                                                 const float *__restrict__ delta,
+                                                                 float *__restrict__ dkt, float *__restrict__ dvt) {
+  using Tile = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  constexpr int QS = D + 8, TS = BQ + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t qs[BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t gs[BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t qts[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t gts[D * TS];
-  __shared__ float ls[BQ], dls[BQ];
+  __shared__ __attribute__((aligned(16))) Tile buf[2];
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
-  const int j0 = kb * BK, kw = j0 + 32 * w, kj = kw + ln;
+  const int j0 = kb * kKvBK, kw = j0 + 32 * w, kj = kw + ln;
   const long long hbS = (long long)h * S;
   const uint16_t *qh = qt + hbS * D;
   const uint16_t *gh = dotb + hbS * D;
   const uint16_t *qth = qtt + (long long)h * D * Sv;
   const uint16_t *gth = dott + (long long)h * D * Sv;
+
+  uint4 rq[Tile::RPT], rg[Tile::RPT], rqt[Tile::RPT], rgt[Tile::RPT];
+  float rl = 0.f;
+  auto load_tile = [&](int q0) {
+#pragma unroll
+    for (int it = 0; it < Tile::RPT; ++it) {
+      const int idx = it * kKvThreads + tid;
+      const int r = idx / (D / 8), cc = idx % (D / 8);
+      const bool ok = q0 + r < S;
+      rq[it] = ok ? *reinterpret_cast<const uint4 *>(qh + (long long)(q0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+      rg[it] = ok ? *reinterpret_cast<const uint4 *>(gh + (long long)(q0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+      const int tr = idx / (kKvBQ / 8), tc = idx % (kKvBQ / 8);
+      rqt[it] = *reinterpret_cast<const uint4 *>(qth + (long long)tr * Sv + q0 + tc * 8);
+      rgt[it] = *reinterpret_cast<const uint4 *>(gth + (long long)tr * Sv + q0 + tc * 8);
+    }
+    if (tid < 2 * kKvBQ) {
+      const int r = tid & (kKvBQ - 1);
+      rl = (q0 + r < S) ? (tid < kKvBQ ? lse[hbS + q0 + r] * kLog2e : delta[hbS + q0 + r]) : 0.f;
+    }
+  };
+  auto store_tile = [&](Tile &t) {
+#pragma unroll
+    for (int it = 0; it < Tile::RPT; ++it) {
+      const int idx = it * kKvThreads + tid;
+      const int r = idx / (D / 8), cc = idx % (D / 8);
+      *reinterpret_cast<uint4 *>(&t.q[r * Tile::QS + cc * 8]) = rq[it];
+      *reinterpret_cast<uint4 *>(&t.g[r * Tile::QS + cc * 8]) = rg[it];
+      const int tr = idx / (kKvBQ / 8), tc = idx % (kKvBQ / 8);
+      st_split8(&t.qt[tr * Tile::TS + tc * 8], rqt[it]);
+      st_split8(&t.gt[tr * Tile::TS + tc * 8], rgt[it]);
+    }
+    if (tid < kKvBQ) t.ls[tid] = rl;
+    else if (tid < 2 * kKvBQ) t.dl[tid - kKvBQ] = rl;
+  };
+
   bf16x8 kf[KC], vf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
@@ -213,45 +292,48 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkdv(int S, int Sv, int BH,
     adk[b] = (f32x16){};
     adv[b] = (f32x16){};
   }
-  for (int q0 = j0; q0 < S; q0 += BQ) {
-    __syncthreads();
-    stage_rows<BQ, D, QS>(qs, qh, q0, S);
-    stage_rows<BQ, D, QS>(gs, gh, q0, S);
-    stage_cols<BQ, D, TS>(qts, qth, q0, S, Sv);
-    stage_cols<BQ, D, TS>(gts, gth, q0, S, Sv);
-    if (tid < BQ) {
-      ls[tid] = (q0 + tid < S) ? lse[hbS + q0 + tid] * kLog2e : 0.f;
-      dls[tid] = (q0 + tid < S) ? delta[hbS + q0 + tid] : 0.f;
-    }
-    __syncthreads();
-    if (q0 + BQ - 1 < kw) continue;   // every query of the tile precedes this wavefront's keys
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+  const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
+  load_tile(j0);
+  store_tile(buf[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    const int q0 = j0 + t * kKvBQ;
+    if (t + 1 < nt) load_tile(q0 + kKvBQ);
+    const Tile &cur = buf[t & 1];
+    if (q0 + kKvBQ - 1 >= kw) {   // otherwise every query of the tile precedes this wavefront's keys
+      f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&qs[ln * QS + 16 * c + 8 * hf]), kf[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&gs[ln * QS + 16 * c + 8 * hf]), vf[c], dp, 0, 0, 0);
-    }
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = 8 * c + j;
-        const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
-        const int q = q0 + r;
-        const float pj = (q >= kj && q < S && kj < S) ? exp2f(fmaf(s[i], c2, -ls[r])) : 0.f;
-        pf[c][j] = (__bf16)pj;
-        dsf[c][j] = (__bf16)(pj * (dp[i] - dls[r]));
+      for (int c = 0; c < KC; ++c) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.q[ln * Tile::QS + 16 * c + 8 * hf]), kf[c], s, 0, 0,
+                                                    0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.g[ln * Tile::QS + 16 * c + 8 * hf]), vf[c], dp, 0,
+                                                     0, 0);
       }
+      const bool diag = q0 < kw + 31;   // some query of the tile precedes some key of the wavefront
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_split8(&gts[(32 * b + ln) * TS + 16 * c + 4 * hf]), pf[c],
-                                                         adv[b], 0, 0, 0);
-        adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_split8(&qts[(32 * b + ln) * TS + 16 * c + 4 * hf]),
-                                                         dsf[c], adk[b], 0, 0, 0);
-      }
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * c + j;
+          const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+          float pj = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -cur.ls[r]));
+          if ((diag && q0 + r < kj) || q0 + r >= S || kj >= S) pj = 0.f;
+          pf[c][j] = (__bf16)pj;
+          dsf[c][j] = (__bf16)(pj * (dp[i] - cur.dl[r]));
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_split8(&cur.gt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), pf[c], adv[b], 0, 0, 0);
+          adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_split8(&cur.qt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), dsf[c], adk[b], 0, 0, 0);
+        }
+    }
+    if (t + 1 < nt) store_tile(buf[(t + 1) & 1]);
+    __syncthreads();
   }
   if (kj >= S) return;
   const float scale = 1.f / sqrtf((float)D);
@@ -278,13 +360,13 @@ hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, co
   const uint16_t *q = (const uint16_t *)qt, *k = (const uint16_t *)kt, *v = (const uint16_t *)vt;
   const uint16_t *qT = (const uint16_t *)qtt, *kT = (const uint16_t *)ktt;
   const uint16_t *g = (const uint16_t *)dotb, *gT = (const uint16_t *)dott;
-  dim3 gq(((S + 127) / 128) * BH), gk(((S + 127) / 128) * BH);
+  dim3 gq(((S + kDqBM - 1) / kDqBM) * BH), gk(((S + kKvBK - 1) / kKvBK) * BH);
   if (d == 128) {
-    k_attn_bwd_dq<128><<<gq, 256, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
-    k_attn_bwd_dkdv<128><<<gk, 256, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
+    k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
+    k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
   } else {
-    k_attn_bwd_dq<64><<<gq, 256, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
-    k_attn_bwd_dkdv<64><<<gk, 256, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
+    k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
+    k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
   }
   return hipGetLastError();
 }
