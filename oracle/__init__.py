@@ -3,6 +3,6 @@ see ``lighthouse_ref`` for what it computes and which passages it follows)."""
 from .lighthouse_ref import *  # noqa: F401,F403
 from .lighthouse_ref import (attend, attend_adjoint, attend_rows, backward_head, budget, coords_of_flat,  # noqa: F401
                              flat_offsets, forward, forward_head, from_fixed, gather, level_sizes,
-                             order, pool_adjoint, pyramid, scatter, scatter_adjoint, scatter_fixed,
+                             order, pool_adjoint, pyramid, round_bf16, scatter, scatter_adjoint, scatter_fixed,
                              scatter_range, scores, select, subsequence_length_eq8, to_fixed,
                              window_end)

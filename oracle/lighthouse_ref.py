@@ -48,7 +48,12 @@ reason, in the repository's design notes):
     among equal ends;
   * the scatter range [end, end + p^l - 1] is clipped at N - 1; positions with no
     selected contributor receive 0;
-  * fixed point: int64 with 32 fractional bits, round-half-even in and out.
+  * fixed point: int64 with 32 fractional bits, round-half-even in and out;
+  * bf16 mode (``store="bf16"``): the paper benchmarks the layer in bf16 and
+    hands the gathered sub-sequence to stock FlashAttention as bf16 tensors
+    (§3.5; experiments paragraph on Fig. 3), so the pooled levels l >= 1 are
+    rounded to bf16 (round to nearest even) once, right after their exact
+    mean; every other step stays fp64.  Level 0 is the bf16 input itself.
 
 Every function here has a pin in tests/ against something other than itself
 (closed forms, a textbook special case, brute force, finite differences).
@@ -98,15 +103,29 @@ def subsequence_length_eq8(N: int, L: int, p: int, k: int) -> int:
 # ----------------------------------------------------------------------------
 # 1. pyramid (Paper §3.3)
 # ----------------------------------------------------------------------------
-def pyramid(x: np.ndarray, L: int, p: int) -> list[np.ndarray]:
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even), returned as float64:
+    keep the top 16 bits of the fp32 pattern after adding half an ulp of bf16
+    (plus one if the kept part is odd).  x must already be an fp32 value or be
+    rounded to fp32 first (done here)."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def pyramid(x: np.ndarray, L: int, p: int, store: str | None = None) -> list[np.ndarray]:
     """Levels 0..L-1 of one tensor x [N, d]: X^(l)_i = mean of x over the
-    base tokens t in [i p^l, (i+1) p^l - 1] (direct mean from level 0)."""
+    base tokens t in [i p^l, (i+1) p^l - 1] (direct mean from level 0).
+    store="bf16" rounds the pooled levels (l >= 1) to bf16 after the mean."""
     x = np.asarray(x, dtype=np.float64)
     N, d = x.shape
     out = []
     for l, n in enumerate(level_sizes(N, L, p)):
         w = p ** l
-        out.append(x.reshape(n, w, d).mean(axis=1))
+        lev = x.reshape(n, w, d).mean(axis=1)
+        if store == "bf16" and l > 0:
+            lev = round_bf16(lev)
+        out.append(lev)
     return out
 
 
@@ -317,13 +336,15 @@ def scatter_fixed(ot: np.ndarray, sorted_flat: np.ndarray, N: int, L: int, p: in
 # ----------------------------------------------------------------------------
 # whole forward for one head (Paper §3.2 four-stage pipeline)
 # ----------------------------------------------------------------------------
-def forward_head(q, k, v, L: int, p: int, topk: int, flags=None, out_dtype: str | None = None):
+def forward_head(q, k, v, L: int, p: int, topk: int, flags=None, out_dtype: str | None = None,
+                 store: str | None = None):
     """One (b, h) head.  q, k, v: [N, d] arrays (any float dtype, upcast to fp64).
 
     ``flags`` (optional) injects a selection instead of computing one.  Returns a
     dict with the pyramid scores, the selection, the sorted flat indices, the
     gathered rows, O~, LSE, the fp64 output O, and (if ``out_dtype`` is given)
-    the fixed-point output."""
+    the fixed-point output.  ``store="bf16"`` rounds the pooled levels to bf16
+    (see the module notes)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -333,7 +354,7 @@ def forward_head(q, k, v, L: int, p: int, topk: int, flags=None, out_dtype: str 
     if flags is None:
         flags = select(qk, kq, p, topk)
     sorted_flat = order(flags, N, L, p)
-    lq, lk, lv = pyramid(q, L, p), pyramid(k, L, p), pyramid(v, L, p)
+    lq, lk, lv = pyramid(q, L, p, store), pyramid(k, L, p, store), pyramid(v, L, p, store)
     qt = gather(lq, sorted_flat, N, L, p)
     kt = gather(lk, sorted_flat, N, L, p)
     vt = gather(lv, sorted_flat, N, L, p)

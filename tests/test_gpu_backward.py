@@ -4,10 +4,10 @@ Two references, both the fp64 oracle with the GPU's selection injected:
   * stage-consistent: the oracle's adjoints (scatter, attention, gather, pool)
     evaluated on the GPU's own gathered rows, so only the kernels' arithmetic
     differs -- bar (relative to the gradient's largest magnitude) 1e-5 in fp32
-    mode (fp32 accumulation over <= S terms) and 3 * 2^-9 in bf16 mode: the
+    mode (fp32 accumulation over <= S terms) and 3 * 2^-8 in bf16 mode: the
     bf16 MFMA backward takes three operands rounded to bf16 (P, dS and dO~, each
-    within 2^-9 relative), and consumes the forward's O~ and LSE, computed from
-    bf16-rounded probabilities;
+    within the bf16 unit roundoff 2^-8, relative), and consumes the forward's O~
+    and LSE, computed from bf16-rounded probabilities;
   * end to end: the oracle's own fp64 pyramid and backward -- bar 2e-2 of the
     gradient's largest magnitude, the forward's bf16 bar applied to the
     gradients' scale (pooled rows are stored in bf16, so the logits of pooled
@@ -24,7 +24,7 @@ from hierarchical_sparse_attention_mean_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-STAGE_TOL = {"f32": 1e-5, "bf16": 3 * 2.0 ** -9}
+STAGE_TOL = {"f32": 1e-5, "bf16": 3 * 2.0 ** -8}
 E2E_TOL = 2e-2
 
 

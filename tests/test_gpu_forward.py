@@ -9,17 +9,21 @@ Bars (from the method's acceptance criteria and the arithmetic):
                        storage dtype (bf16: 2^-8 relative, fp32: 2e-6) of the fp64 mean
   O~, LSE              fp32 mode 1e-4 (the end-to-end fp32 bar: with rows scaled
                        x4 the logits reach |z| ~ 30, so fp32 logits carry ~1e-5
-                       relative error into the softmax weights); bf16 mode 1e-2
-                       (the P.V product takes P
-                       rounded to bf16: each weight off by <= 2^-9 relative, so
-                       |dO~| <= 2^-9 max|V|), against the oracle run on the GPU's
-                       own gathered rows
+                       relative error into the softmax weights); bf16 mode
+                       2^-8 max|V~| + 1e-4 (the P.V product takes P rounded to
+                       bf16: each weight off by at most the bf16 unit roundoff
+                       2^-8, relative, so |dO~| <= 2^-8 sum_j P_j |V~_j| <=
+                       2^-8 max|V~|), against the oracle run on the GPU's own
+                       gathered rows
   scatter              bit-exact against the oracle's fixed-point scatter of the
                        GPU's own O~
   O end to end         1e-4 max-abs (fp32) / 2e-2 max-abs (bf16) against the oracle
-                       on the same inputs; if fp64 and fp32 scores order a near-tie
-                       differently the oracle is re-run with the GPU's selection
-                       injected (the size of the difference is printed)
+                       on the same inputs; in bf16 mode the oracle stores the
+                       pooled levels in bf16 like the benchmarked bf16 layer
+                       (store="bf16"), and the pure-fp64 error is printed too; if
+                       fp64 and fp32 scores order a near-tie differently the
+                       oracle is re-run with the GPU's selection injected (the
+                       size of the difference is printed)
 """
 import numpy as np
 import pytest
@@ -30,7 +34,10 @@ from hierarchical_sparse_attention_mean_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-STAGE_OT_TOL = {"f32": 1e-4, "bf16": 1e-2}
+def stage_ot_tol(dt, vt):
+    return 1e-4 if dt == "f32" else 2.0 ** -8 * float(np.max(np.abs(vt))) + 1e-4
+
+
 LSE_TOL = {"f32": 1e-4, "bf16": 1e-3}
 E2E_TOL = {"f32": 1e-4, "bf16": 2e-2}
 
@@ -75,20 +82,25 @@ def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True,
     err_ot = np.max(np.abs(g["ot32"][rows].astype(np.float64) - ot_ref))
     err_lse = np.max(np.abs(g["lse"][rows] - lse_ref))
     say(f"  head {h}: S={S} |O~ - oracle(O~)|={err_ot:.3e} |LSE - oracle|={err_lse:.3e}")
-    assert err_ot <= STAGE_OT_TOL[dt]
+    assert err_ot <= stage_ot_tol(dt, g["vt"])
     assert err_lse <= LSE_TOL[dt]
     # ---- scatter: bit-exact on the GPU's own O~
     o_fx = orc.scatter_fixed(g["ot32"].astype(np.float64), sf, N, L, p, out_dtype)
     assert np.array_equal(o_fx, g["o"]), "scatter not bit-exact"
     # ---- end to end
     if e2e:
-        res = orc.forward_head(q64, k64, v64, L, p, topk)
+        store = "bf16" if dt == "bf16" else None
+        res = orc.forward_head(q64, k64, v64, L, p, topk, store=store)
         nd = int(np.sum(res["flags"] != g["flags"]))
         if nd:
             say(f"  head {h}: oracle fp64 selection differs from GPU's in {nd} entries; injecting GPU selection")
-            res = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"])
+            res = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"], store=store)
         err = np.max(np.abs(res["o"] - g["o"]))
-        say(f"  head {h}: end-to-end |O - oracle O| = {err:.3e}")
+        msg = f"  head {h}: end-to-end |O - oracle O| = {err:.3e}"
+        if store:
+            pure = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"])
+            msg += f" (pure-fp64 pyramid: {np.max(np.abs(pure['o'] - g['o'])):.3e})"
+        say(msg)
         assert err <= E2E_TOL[dt] + (2.0 ** -8 * np.max(np.abs(res["o"])) if out_dtype == "bf16" else 0.0)
     return S
 

@@ -451,3 +451,23 @@ def test_attend_rows_matches_attend():
     o2, lse2 = orc.attend_rows(qt, kt, vt, rows)
     assert np.max(np.abs(o2 - o[rows])) < 1e-13
     assert np.max(np.abs(lse2 - lse[rows])) < 1e-13
+
+
+def test_round_bf16_cases():
+    """bf16 keeps 8 significant bits: 1 + 2^-8 is a tie between 1 and 1 + 2^-7
+    (to even: 1); 1 + 3 * 2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6 (to even:
+    1 + 2^-6); just above the half-ulp rounds up; sign and powers of two exact."""
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -3.0, 2.0 ** -100, 0.0])
+    assert orc.round_bf16(x).tolist() == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -3.0, 2.0 ** -100, 0.0]
+
+
+def test_pyramid_bf16_store_rounds_only_pooled_levels():
+    rng = np.random.default_rng(16)
+    x = orc.round_bf16(rng.standard_normal((64, 5)))
+    a = orc.pyramid(x, 3, 4)
+    b = orc.pyramid(x, 3, 4, store="bf16")
+    assert np.array_equal(a[0], b[0])
+    for u, w in zip(a[1:], b[1:]):
+        # bf16 keeps 8 significant bits: unit roundoff 2^-8 (after the fp32 rounding)
+        assert np.all(np.abs(u - w) <= (2.0 ** -8 + 2.0 ** -23) * np.abs(u))
+        assert np.array_equal(orc.round_bf16(w), w)                # already bf16 values
