@@ -178,7 +178,12 @@ def main() -> int:
     extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "attn_fwd_kernel_ms": attn_ms,
              "attn_fwd_flops": flops, "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
     if args.dense:
-        vt_dense = v.reshape(BH, N, d).transpose(1, 2).contiguous() if io == torch.bfloat16 else v.reshape(BH, N, d)
+        if io == torch.bfloat16:   # V^T, columns in the kernel's order (bits 2 and 3 of the index swapped)
+            col = torch.arange(N, device=dev)
+            perm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1)
+            vt_dense = v.reshape(BH, N, d).transpose(1, 2)[:, :, perm].contiguous()
+        else:
+            vt_dense = v.reshape(BH, N, d)
         od = torch.empty((BH, N, d), dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)

@@ -1,0 +1,72 @@
+// Tile staging shared by the bf16 MFMA attention kernels (gfx950).
+//
+// Tiles go from global memory straight into LDS with global_load_lds_dwordx4:
+// each lane of a wavefront fetches 16 bytes from an address of its own and the
+// hardware writes them at (LDS base) + 16 * lane, so one instruction fills one
+// contiguous 1 KB block and no registers hold the data in flight.  Since the
+// blocks are contiguous, LDS rows cannot be padded; bank conflicts are avoided
+// instead by XOR-swizzling the 16-byte chunks of each row: logical chunk c of
+// row r is stored at chunk c ^ swz(r), chosen so that 8 consecutive rows put
+// the same logical chunk in 8 different 16-byte bank groups.
+//
+// MFMA operand reads (v_mfma_f32_32x32x16_bf16): lane (ln, hf) = (lane % 32,
+// lane / 32) reads row ln of a 32-row block, logical chunk 2c + hf, i.e. the 8
+// consecutive contraction elements 16c + 8hf .. +7 -- for row-major tiles
+// (contraction over d) directly.  Transposed tiles (contraction over keys or
+// queries) are stored by their producers with bits 2 and 3 of the column index
+// swapped (see perm16), which turns the MFMA's split k-chunk
+// {16c + 4hf + 0..3, 16c + 8 + 4hf + 0..3} -- forced by the 32x32 result
+// layout of the probabilities -- into the same single 16-byte read.
+#pragma once
+
+#include "lh_internal.h"
+
+namespace lh {
+namespace tiles {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// column position of element m in a transposed copy: bits 2 and 3 swapped
+__host__ __device__ __forceinline__ int perm16(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// chunk swizzle for rows of W bytes
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  return W >= 128 ? (r & 7) : ((r >> 1) & 3);
+}
+
+// byte offset of (row r, logical 16-byte chunk c) in a tile of W-byte rows
+template <int W>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * W + 16 * (c ^ swz<W>(r));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char *tile, int off) {
+  return *reinterpret_cast<const bf16x8 *>(tile + off);
+}
+
+// Fill an R x W-byte tile: row r comes from gsrc + min(r, rclamp) * gstride.
+// Every wavefront of the NT-thread work-group issues its share of 1 KB blocks.
+template <int W, int R, int NT>
+__device__ __forceinline__ void dma_tile(char *lds_tile, const char *gsrc, long long gstride, int rclamp) {
+  constexpr int BLOCKS = R * W / 1024;
+  static_assert(R * W % 1024 == 0, "tile must be whole 1 KB blocks");
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int b = w; b < BLOCKS; b += NT / 64) {
+    const int byte = b * 1024 + 16 * l;
+    const int r = byte / W;
+    const int pc = (byte % W) / 16;
+    const int lc = pc ^ swz<W>(r);
+    const char *src = gsrc + (long long)min(r, rclamp) * gstride + 16 * lc;
+    __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(lds_tile + b * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// wait for this wavefront's outstanding global loads (the LDS fills included)
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
+}  // namespace tiles
+}  // namespace lh

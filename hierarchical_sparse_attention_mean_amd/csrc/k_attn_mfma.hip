@@ -13,12 +13,14 @@
 // (converted to bf16) are then the B operand, straight from registers, of
 // O^T += V~^T P^T, whose result again gives each lane one query column -- the
 // running max, sum and rescale factor are per-lane scalars.  V~^T comes
-// pre-transposed from the gather ([d][Sv], Sv a multiple of 64, zero padded) so
-// both LDS operands are read as contiguous rows.
+// pre-transposed from the gather ([d][Sv], Sv a multiple of 64, zero padded,
+// columns in the perm16 order of attn_tiles.h) so both LDS operands are single
+// 16-byte reads per lane.
 //
 // Work-group: 8 wavefronts x 32 queries = 256 query rows (one work-group per
-// CU); key/value tiles of 64 rows, double-buffered in LDS, the next tile's
-// global loads in flight in registers while the current tile is computed.
+// CU); key/value tiles of 64 rows, double-buffered in LDS and filled by direct
+// global->LDS loads (attn_tiles.h): the next tile streams in while the current
+// one is computed, with no registers spent on it.
 // Softmax: exp2 with log2(e)/sqrt(d) folded into one FMA; the accumulators are
 // rescaled only on tiles where some lane's running max grows (after the first
 // few tiles most do not).  The running max is kept exact, so each row's
@@ -26,15 +28,14 @@
 // of P.  Work-groups are numbered head-fastest (block b -> head b mod BH)
 // and longest query blocks first: with BH a multiple of 8 a head's blocks share
 // one XCD's L2, and the causal tail is balanced.
-#include "lh_internal.h"
+#include "attn_tiles.h"
 
 namespace lh {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using tiles::bf16x8;
+using tiles::f32x16;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -45,25 +46,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
 struct FwdTile {
-  static constexpr int KS = D + 8;              // padded K~ row stride (bf16)
-  static constexpr int VS = BN + 4;             // padded V~^T row stride (bf16)
-  static constexpr int KCH = BN * D / 8;        // 16-byte chunks per K~ tile
-  static constexpr int VCH = D * BN / 8;        // 16-byte chunks per V~^T tile
-  static constexpr int KPT = KCH / kThreads;    // chunks per thread
-  static constexpr int VPT = VCH / kThreads;
-  uint16_t k[BN * KS];
-  uint16_t v[D * VS];
+  static constexpr int WK = 2 * D;    // bytes per K~ row
+  static constexpr int WV = 2 * BN;   // bytes per V~^T row
+  char k[BN * WK];
+  char v[D * WV];
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, int BH, const uint16_t *__restrict__ qt,
+__global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sq, int Sv, int BH,
+                                                               const uint16_t *__restrict__ qt,
                                                                const uint16_t *__restrict__ kt,
                                                                const uint16_t *__restrict__ vtt,
                                                                float *__restrict__ ot, float *__restrict__ lse) {
   using Tile = FwdTile<D>;
   constexpr int KC = D / 16;   // 16-wide d chunks of the Q.K contraction
   constexpr int DB = D / 32;   // 32-row d blocks of O^T
-  __shared__ __attribute__((aligned(16))) Tile buf[2];
+  __shared__ __attribute__((aligned(1024))) Tile buf[2];
 
   const int nqb = (S + BM - 1) / BM;
   const int h = blockIdx.x % BH;
@@ -73,43 +71,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, in
   const int q0 = qb * BM;
   const int qw = q0 + 32 * w;   // first query of this wavefront
   const int qi = qw + ln;       // this lane's query
-  const long long hbS = (long long)h * S;
-  const uint16_t *qh = qt + hbS * D;
-  const uint16_t *kh = kt + hbS * D;
-  const uint16_t *vh = vtt + (long long)h * D * Sv;
+  const long long hbS = (long long)h * S;   // O~, LSE: S rows per head
+  const uint16_t *qh = qt + (long long)h * Sq * D;   // Q~, K~: Sq rows per head
+  const char *kh = reinterpret_cast<const char *>(kt + (long long)h * Sq * D);
+  const char *vh = reinterpret_cast<const char *>(vtt + (long long)h * D * Sv);
 
-  // global -> registers for one tile (rows past S read as zero)
-  uint4 kreg[Tile::KPT], vreg[Tile::VPT];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int it = 0; it < Tile::KPT; ++it) {
-      const int idx = it * kThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      kreg[it] = (k0 + r < S) ? *reinterpret_cast<const uint4 *>(kh + (long long)(k0 + r) * D + cc * 8)
-                              : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < Tile::VPT; ++it) {
-      const int idx = it * kThreads + tid;
-      const int r = idx / (BN / 8), cc = idx % (BN / 8);   // r = d row, cc = 8-key chunk
-      vreg[it] = *reinterpret_cast<const uint4 *>(vh + (long long)r * Sv + k0 + cc * 8);
-    }
-  };
-  auto store_tile = [&](Tile &t) {
-#pragma unroll
-    for (int it = 0; it < Tile::KPT; ++it) {
-      const int idx = it * kThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      *reinterpret_cast<uint4 *>(&t.k[r * Tile::KS + cc * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < Tile::VPT; ++it) {
-      const int idx = it * kThreads + tid;
-      const int r = idx / (BN / 8), cc = idx % (BN / 8);
-      uint2 *dst = reinterpret_cast<uint2 *>(&t.v[r * Tile::VS + cc * 8]);
-      dst[0] = make_uint2(vreg[it].x, vreg[it].y);
-      dst[1] = make_uint2(vreg[it].z, vreg[it].w);
-    }
+  // K~ rows past S are clamped to row S-1 (finite; those keys are causally masked);
+  // V~^T columns past S are the zero padding up to Sv.
+  auto fill = [&](Tile &t, int k0) {
+    tiles::dma_tile<Tile::WK, BN, kThreads>(t.k, kh + (long long)k0 * Tile::WK, Tile::WK, S - 1 - k0);
+    tiles::dma_tile<Tile::WV, D, kThreads>(t.v, vh + 2LL * k0, 2LL * Sv, D - 1);
   };
 
   // Q~ fragment: B operand of S^T = K~ Q~^T (lane: query qi, d = 16c + 8hf .. +7)
@@ -126,12 +97,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, in
 
   const int kend = min(S, q0 + BM);
   const int nt = (kend + BN - 1) / BN;
-  load_tile(0);
-  store_tile(buf[0]);
+  fill(buf[0], 0);
+  tiles::dma_wait();
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     const int k0 = t * BN;
-    if (t + 1 < nt) load_tile(k0 + BN);
+    if (t + 1 < nt) fill(buf[(t + 1) & 1], k0 + BN);   // streams in while this tile is computed
     const Tile &cur = buf[t & 1];
     if (k0 <= qw + 31) {   // otherwise the whole tile is in this wavefront's future
       f32x16 st[2];
@@ -139,10 +110,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, in
       for (int kb = 0; kb < 2; ++kb) {
         st[kb] = (f32x16){};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.k[(32 * kb + ln) * Tile::KS + 16 * c + 8 * hf]);
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], st[kb], 0, 0, 0);
-        }
+        for (int c = 0; c < KC; ++c)
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tiles::lds_frag(cur.k, tiles::tile_off<Tile::WK>(32 * kb + ln, 2 * c + hf)), qf[c], st[kb], 0, 0, 0);
       }
       if (k0 + BN - 1 > qw) {   // tile reaches past this wavefront's first query: causal mask
 #pragma unroll
@@ -183,15 +153,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, in
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const uint16_t *row = &cur.v[(32 * b + ln) * Tile::VS + 16 * c + 4 * hf];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + 8);
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc[b], 0, 0, 0);
-        }
+        for (int b = 0; b < DB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tiles::lds_frag(cur.v, tiles::tile_off<Tile::WV>(32 * b + ln, 2 * c + hf)), pf[c], acc[b], 0, 0, 0);
     }
-    if (t + 1 < nt) store_tile(buf[(t + 1) & 1]);
+    tiles::dma_wait();
     __syncthreads();
   }
   if (qi >= S) return;
@@ -211,15 +177,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sv, in
 
 }  // namespace
 
-hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int vstride, const void *qt, const void *kt, const void *vtt,
+hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, int vstride, const void *qt, const void *kt, const void *vtt,
                                 float *ot, float *lse, hipStream_t st) {
   const int nqb = (S + BM - 1) / BM;
   dim3 grid(nqb * BH);
   if (d == 128)
-    k_attn_fwd_mfma<128><<<grid, kThreads, 0, st>>>(S, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+    k_attn_fwd_mfma<128><<<grid, kThreads, 0, st>>>(S, Sq, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
                                                     (const uint16_t *)vtt, ot, lse);
   else
-    k_attn_fwd_mfma<64><<<grid, kThreads, 0, st>>>(S, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+    k_attn_fwd_mfma<64><<<grid, kThreads, 0, st>>>(S, Sq, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
                                                    (const uint16_t *)vtt, ot, lse);
   return hipGetLastError();
 }

@@ -14,43 +14,30 @@
 //                    dP^T = V~ dO~^T (lane = one query), dS^T in registers, and
 //                    accumulates dQ^T += K~^T dS^T with K~^T from LDS.
 //                    8 wavefronts, 256 queries per work-group.
-//   k_attn_bwd_dkdv  key-stationary: a wavefront holds 32 key rows of K~ and V~
-//                    as B operands; per query tile it forms S = Q~ K~^T and
+//   k_attn_bwd_dkdv  key-stationary: the work-group's 128 K~ and V~ rows sit in
+//                    LDS as B operands; per query tile it forms S = Q~ K~^T and
 //                    dP = dO~ V~^T (lane = one key), and accumulates
 //                    dV^T += dO~^T P and dK^T += Q~^T dS with the transposed
 //                    query-side operands from LDS.  4 wavefronts, 128 keys per
 //                    work-group (the accumulators need the register file of a
 //                    whole SIMD).
-// Both stream their tiles through double-buffered LDS with the next tile's
-// global loads in flight in registers.  The transposed operands (K~^T, Q~^T,
-// dO~^T; row stride Sv, a multiple of 64, zero padded) are written by the
-// gather and by the scatter adjoint, so every LDS operand is read as rows.
-#include "lh_internal.h"
+// Both stream their tiles through double-buffered LDS, filled by direct
+// global->LDS loads (attn_tiles.h) while the previous tile is computed.  The
+// transposed operands (K~^T, Q~^T, dO~^T; row stride Sv, a multiple of 64,
+// zero padded, columns in perm16 order) are written by the gather and by the
+// scatter adjoint, so every LDS operand is one 16-byte read per lane.  The
+// row-major operands are padded with zero rows up to Sv, so no tile load needs a
+// bounds check: a padding query or key contributes exactly 0.
+#include "attn_tiles.h"
 
 namespace lh {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using tiles::bf16x8;
+using tiles::f32x16;
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-// two 4-element pieces 8 apart: the k-chunk mapping (h, j) -> 8 (j/4) + 4 h + j%4
-__device__ __forceinline__ bf16x8 lds_split8(const uint16_t *p) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 8);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ void st_split8(uint16_t *p, uint4 v) {
-  uint2 *d2 = reinterpret_cast<uint2 *>(p);
-  d2[0] = make_uint2(v.x, v.y);
-  d2[1] = make_uint2(v.z, v.w);
-}
 
 // ---------------------------------------------------------------------------
 // dQ
@@ -62,13 +49,11 @@ constexpr int kDqBN = 64;
 
 template <int D>
 struct DqTile {
-  static constexpr int KS = D + 8;
-  static constexpr int TS = kDqBN + 4;
-  static constexpr int RCH = kDqBN * D / 8;          // 16-byte chunks of one row tile
-  static constexpr int RPT = RCH / kDqThreads;       // per thread
-  uint16_t k[kDqBN * KS];
-  uint16_t v[kDqBN * KS];
-  uint16_t kt[D * TS];
+  static constexpr int WR = 2 * D;       // bytes per K~ / V~ row
+  static constexpr int WT = 2 * kDqBN;   // bytes per K~^T row
+  char k[kDqBN * WR];
+  char v[kDqBN * WR];
+  char kt[D * WT];
 };
 
 template <int D>
@@ -82,48 +67,31 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
                                                                float *__restrict__ dqt) {
   using Tile = DqTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) Tile buf[2];
+  __shared__ __attribute__((aligned(1024))) Tile buf[2];
   const int nqb = (S + kDqBM - 1) / kDqBM;
   const int h = blockIdx.x % BH;
   const int qb = nqb - 1 - blockIdx.x / BH;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int q0 = qb * kDqBM, qw = q0 + 32 * w, qi = qw + ln;
-  const long long hbS = (long long)h * S;
-  const uint16_t *kh = kt + hbS * D;
-  const uint16_t *vh = vt + hbS * D;
-  const uint16_t *kth = ktt + (long long)h * D * Sv;
+  const long long hbS = (long long)h * S;    // LSE, delta, dQ~: S rows per head
+  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~: Sv rows per head (rows S..Sv-1 zero)
+  const char *kh = reinterpret_cast<const char *>(kt + hbV * D);
+  const char *vh = reinterpret_cast<const char *>(vt + hbV * D);
+  const char *kth = reinterpret_cast<const char *>(ktt + (long long)h * D * Sv);
 
-  uint4 rk[Tile::RPT], rv[Tile::RPT], rt[Tile::RPT];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int it = 0; it < Tile::RPT; ++it) {
-      const int idx = it * kDqThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      const bool ok = k0 + r < S;
-      rk[it] = ok ? *reinterpret_cast<const uint4 *>(kh + (long long)(k0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
-      rv[it] = ok ? *reinterpret_cast<const uint4 *>(vh + (long long)(k0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
-      const int tr = idx / (kDqBN / 8), tc = idx % (kDqBN / 8);
-      rt[it] = *reinterpret_cast<const uint4 *>(kth + (long long)tr * Sv + k0 + tc * 8);
-    }
-  };
-  auto store_tile = [&](Tile &t) {
-#pragma unroll
-    for (int it = 0; it < Tile::RPT; ++it) {
-      const int idx = it * kDqThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      *reinterpret_cast<uint4 *>(&t.k[r * Tile::KS + cc * 8]) = rk[it];
-      *reinterpret_cast<uint4 *>(&t.v[r * Tile::KS + cc * 8]) = rv[it];
-      const int tr = idx / (kDqBN / 8), tc = idx % (kDqBN / 8);
-      st_split8(&t.kt[tr * Tile::TS + tc * 8], rt[it]);
-    }
+  // key tiles start below S and are 64 rows: they never pass the padded Sv rows
+  auto fill = [&](Tile &t, int k0) {
+    tiles::dma_tile<Tile::WR, kDqBN, kDqThreads>(t.k, kh + (long long)k0 * Tile::WR, Tile::WR, kDqBN - 1);
+    tiles::dma_tile<Tile::WR, kDqBN, kDqThreads>(t.v, vh + (long long)k0 * Tile::WR, Tile::WR, kDqBN - 1);
+    tiles::dma_tile<Tile::WT, D, kDqThreads>(t.kt, kth + 2LL * k0, 2LL * Sv, D - 1);
   };
 
   bf16x8 qf[KC], gf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    if (qi < S) {
-      qf[c] = *reinterpret_cast<const bf16x8 *>(qt + (hbS + qi) * D + 16 * c + 8 * hf);
-      gf[c] = *reinterpret_cast<const bf16x8 *>(dotb + (hbS + qi) * D + 16 * c + 8 * hf);
+    if (qi < Sv) {
+      qf[c] = *reinterpret_cast<const bf16x8 *>(qt + (hbV + qi) * D + 16 * c + 8 * hf);
+      gf[c] = *reinterpret_cast<const bf16x8 *>(dotb + (hbV + qi) * D + 16 * c + 8 * hf);
     } else {
       qf[c] = (bf16x8){};
       gf[c] = (bf16x8){};
@@ -138,14 +106,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 
   const int kend = min(S, q0 + kDqBM);
   const int nt = (kend + kDqBN - 1) / kDqBN;
-  load_tile(0);
-  store_tile(buf[0]);
+  fill(buf[0], 0);
+  tiles::dma_wait();
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     const int k0 = t * kDqBN;
-    if (t + 1 < nt) load_tile(k0 + kDqBN);
+    if (t + 1 < nt) fill(buf[(t + 1) & 1], k0 + kDqBN);
     const Tile &cur = buf[t & 1];
-    if (k0 <= qw + 31) {
+    if (k0 <= qw + 31) {   // otherwise the tile is in this wavefront's future
       f32x16 st[2], dp[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -153,13 +121,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
         dp[kb] = (f32x16){};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.k[(32 * kb + ln) * Tile::KS + 16 * c + 8 * hf]),
-                                                           qf[c], st[kb], 0, 0, 0);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.v[(32 * kb + ln) * Tile::KS + 16 * c + 8 * hf]),
-                                                           gf[c], dp[kb], 0, 0, 0);
+          const int off = tiles::tile_off<Tile::WR>(32 * kb + ln, 2 * c + hf);
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.k, off), qf[c], st[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.v, off), gf[c], dp[kb], 0, 0, 0);
         }
       }
-      const bool diag = k0 + kDqBN - 1 > qw;
+      const bool diag = k0 + kDqBN - 1 > qw;   // causal mask (also masks the zero padding keys)
       bf16x8 dsf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -176,9 +143,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 #pragma unroll
         for (int b = 0; b < DB; ++b)
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_split8(&cur.kt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), dsf[c], acc[b], 0, 0, 0);
+              tiles::lds_frag(cur.kt, tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf)), dsf[c], acc[b], 0, 0, 0);
     }
-    if (t + 1 < nt) store_tile(buf[(t + 1) & 1]);
+    tiles::dma_wait();
     __syncthreads();
   }
   if (qi >= S) return;
@@ -204,14 +171,12 @@ constexpr int kKvBQ = 32;
 
 template <int D>
 struct DkvTile {
-  static constexpr int QS = D + 8;
-  static constexpr int TS = kKvBQ + 4;
-  static constexpr int RCH = kKvBQ * D / 8;
-  static constexpr int RPT = RCH / kKvThreads;
-  uint16_t q[kKvBQ * QS];
-  uint16_t g[kKvBQ * QS];
-  uint16_t qt[D * TS];
-  uint16_t gt[D * TS];
+  static constexpr int WR = 2 * D;       // bytes per Q~ / dO~ row
+  static constexpr int WT = 2 * kKvBQ;   // bytes per Q~^T / dO~^T row
+  char q[kKvBQ * WR];
+  char g[kKvBQ * WR];
+  char qt[D * WT];
+  char gt[D * WT];
   float ls[kKvBQ];
   float dl[kKvBQ];
 };
@@ -229,62 +194,43 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
                                                                  float *__restrict__ dkt, float *__restrict__ dvt) {
   using Tile = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) Tile buf[2];
+  __shared__ __attribute__((aligned(1024))) Tile buf[2];
+  // K~ and V~ rows of this work-group's keys, loaded once (B operands of S and dP)
+  __shared__ __attribute__((aligned(1024))) char kv[2][kKvBK * Tile::WR];
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int j0 = kb * kKvBK, kw = j0 + 32 * w, kj = kw + ln;
-  const long long hbS = (long long)h * S;
-  const uint16_t *qh = qt + hbS * D;
-  const uint16_t *gh = dotb + hbS * D;
-  const uint16_t *qth = qtt + (long long)h * D * Sv;
-  const uint16_t *gth = dott + (long long)h * D * Sv;
+  const long long hbS = (long long)h * S;    // LSE, delta, dK~, dV~: S rows per head
+  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~: Sv rows per head (rows S..Sv-1 zero)
+  const char *qh = reinterpret_cast<const char *>(qt + hbV * D);
+  const char *gh = reinterpret_cast<const char *>(dotb + hbV * D);
+  const char *qth = reinterpret_cast<const char *>(qtt + (long long)h * D * Sv);
+  const char *gth = reinterpret_cast<const char *>(dott + (long long)h * D * Sv);
 
-  uint4 rq[Tile::RPT], rg[Tile::RPT], rqt[Tile::RPT], rgt[Tile::RPT];
+  // query tiles start below S and are 32 rows: they never pass the padded Sv
+  // rows.  A padding query has zero Q~ and dO~ rows, so it adds exactly 0.
   float rl = 0.f;
-  auto load_tile = [&](int q0) {
-#pragma unroll
-    for (int it = 0; it < Tile::RPT; ++it) {
-      const int idx = it * kKvThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      const bool ok = q0 + r < S;
-      rq[it] = ok ? *reinterpret_cast<const uint4 *>(qh + (long long)(q0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
-      rg[it] = ok ? *reinterpret_cast<const uint4 *>(gh + (long long)(q0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
-      const int tr = idx / (kKvBQ / 8), tc = idx % (kKvBQ / 8);
-      rqt[it] = *reinterpret_cast<const uint4 *>(qth + (long long)tr * Sv + q0 + tc * 8);
-      rgt[it] = *reinterpret_cast<const uint4 *>(gth + (long long)tr * Sv + q0 + tc * 8);
-    }
+  auto fill = [&](Tile &t, int q0) {
+    tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.q, qh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
+    tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.g, gh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
+    tiles::dma_tile<Tile::WT, D, kKvThreads>(t.qt, qth + 2LL * q0, 2LL * Sv, D - 1);
+    tiles::dma_tile<Tile::WT, D, kKvThreads>(t.gt, gth + 2LL * q0, 2LL * Sv, D - 1);
     if (tid < 2 * kKvBQ) {
       const int r = tid & (kKvBQ - 1);
       rl = (q0 + r < S) ? (tid < kKvBQ ? lse[hbS + q0 + r] * kLog2e : delta[hbS + q0 + r]) : 0.f;
     }
   };
-  auto store_tile = [&](Tile &t) {
-#pragma unroll
-    for (int it = 0; it < Tile::RPT; ++it) {
-      const int idx = it * kKvThreads + tid;
-      const int r = idx / (D / 8), cc = idx % (D / 8);
-      *reinterpret_cast<uint4 *>(&t.q[r * Tile::QS + cc * 8]) = rq[it];
-      *reinterpret_cast<uint4 *>(&t.g[r * Tile::QS + cc * 8]) = rg[it];
-      const int tr = idx / (kKvBQ / 8), tc = idx % (kKvBQ / 8);
-      st_split8(&t.qt[tr * Tile::TS + tc * 8], rqt[it]);
-      st_split8(&t.gt[tr * Tile::TS + tc * 8], rgt[it]);
-    }
+  auto put_rows = [&](Tile &t) {
     if (tid < kKvBQ) t.ls[tid] = rl;
     else if (tid < 2 * kKvBQ) t.dl[tid - kKvBQ] = rl;
   };
 
-  bf16x8 kf[KC], vf[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (kj < S) {
-      kf[c] = *reinterpret_cast<const bf16x8 *>(kt + (hbS + kj) * D + 16 * c + 8 * hf);
-      vf[c] = *reinterpret_cast<const bf16x8 *>(vt + (hbS + kj) * D + 16 * c + 8 * hf);
-    } else {
-      kf[c] = (bf16x8){};
-      vf[c] = (bf16x8){};
-    }
-  }
+  // keys past Sv (last block) read the last padding row, which is zero
+  tiles::dma_tile<Tile::WR, kKvBK, kKvThreads>(kv[0], reinterpret_cast<const char *>(kt + (hbV + j0) * D), Tile::WR,
+                                               Sv - 1 - j0);
+  tiles::dma_tile<Tile::WR, kKvBK, kKvThreads>(kv[1], reinterpret_cast<const char *>(vt + (hbV + j0) * D), Tile::WR,
+                                               Sv - 1 - j0);
   const float c2 = kLog2e / sqrtf((float)D);
   f32x16 adk[DB], adv[DB];
 #pragma unroll
@@ -293,46 +239,60 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     adv[b] = (f32x16){};
   }
   const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
-  load_tile(j0);
-  store_tile(buf[0]);
+  fill(buf[0], j0);
+  put_rows(buf[0]);
+  tiles::dma_wait();
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     const int q0 = j0 + t * kKvBQ;
-    if (t + 1 < nt) load_tile(q0 + kKvBQ);
+    if (t + 1 < nt) fill(buf[(t + 1) & 1], q0 + kKvBQ);
     const Tile &cur = buf[t & 1];
-    if (q0 + kKvBQ - 1 >= kw) {   // otherwise every query of the tile precedes this wavefront's keys
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+    // Every wavefront updates its accumulators on every tile (a conditional
+    // update would make them branch-merged values that the compiler keeps out
+    // of the accumulator registers); tiles before this wavefront's keys are
+    // diagonal-masked to zero, which costs at most 3 tiles per wavefront.
+    {
+      f32x16 sv = (f32x16){}, dp = (f32x16){};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.q[ln * Tile::QS + 16 * c + 8 * hf]), kf[c], s, 0, 0,
-                                                    0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row8(&cur.g[ln * Tile::QS + 16 * c + 8 * hf]), vf[c], dp, 0,
+        const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
+        const int koff = tiles::tile_off<Tile::WR>(32 * w + ln, 2 * c + hf);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.q, off), tiles::lds_frag(kv[0], koff), sv, 0,
+                                                     0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.g, off), tiles::lds_frag(kv[1], koff), dp, 0,
                                                      0, 0);
       }
-      const bool diag = q0 < kw + 31;   // some query of the tile precedes some key of the wavefront
+      // phase boundaries: keep each phase's LDS operand reads inside it (bounded live ranges)
+      __builtin_amdgcn_sched_barrier(0);
+      const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
       bf16x8 pf[2], dsf[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 l4 = *reinterpret_cast<const float4 *>(&cur.ls[8 * g4 + 4 * hf]);
+        const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[8 * g4 + 4 * hf]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * c + j;
-          const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
-          float pj = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -cur.ls[r]));
-          if ((diag && q0 + r < kj) || q0 + r >= S || kj >= S) pj = 0.f;
-          pf[c][j] = (__bf16)pj;
-          dsf[c][j] = (__bf16)(pj * (dp[i] - cur.dl[r]));
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv[e]));
+          if (diag && q0 + 8 * g4 + 4 * hf + e < kj) pj = 0.f;
+          pf[i >> 3][i & 7] = (__bf16)pj;
+          dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv4[e]));
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_split8(&cur.gt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), pf[c], adv[b], 0, 0, 0);
-          adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_split8(&cur.qt[(32 * b + ln) * Tile::TS + 16 * c + 4 * hf]), dsf[c], adk[b], 0, 0, 0);
+          const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf);
+          adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.gt, off), pf[c], adv[b], 0, 0, 0);
+          adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.qt, off), dsf[c], adk[b], 0, 0, 0);
         }
     }
-    if (t + 1 < nt) store_tile(buf[(t + 1) & 1]);
+    if (t + 1 < nt) put_rows(buf[(t + 1) & 1]);
+    tiles::dma_wait();
     __syncthreads();
   }
   if (kj >= S) return;

@@ -31,7 +31,7 @@ __device__ __forceinline__ void stage_rows(float (*dst)[D + 4], const T *src, lo
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_attn_fwd_valu(int S, const T *__restrict__ qt, const T *__restrict__ kt,
+__global__ __launch_bounds__(256) void k_attn_fwd_valu(int S, int Sq, const T *__restrict__ qt, const T *__restrict__ kt,
                                                        const T *__restrict__ vt, float *__restrict__ ot,
                                                        float *__restrict__ lse) {
   constexpr int DP = D / 4;
@@ -45,20 +45,21 @@ __global__ __launch_bounds__(256) void k_attn_fwd_valu(int S, const T *__restric
   const int part = threadIdx.x & 3;
   const int qi = q0 + r;
   const bool active = qi < S;
-  const long long hb = (long long)h * S;
+  const long long hb = (long long)h * S;    // O~, LSE, dO~, gradients: S rows per head
+  const long long hq = (long long)h * Sq;   // gathered Q~, K~, V~: Sq rows per head
   const float scale = kLog2e / sqrtf((float)D);
   float qv[DP], o[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    qv[e] = active ? IO<T>::ld(qt, (hb + qi) * D + part * DP + e) * scale : 0.f;
+    qv[e] = active ? IO<T>::ld(qt, (hq + qi) * D + part * DP + e) * scale : 0.f;
     o[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const int kend = min(S, q0 + BM);
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
-    stage_rows<T, D>(ks, kt + hb * D, k0, min(BN, S - k0));
-    stage_rows<T, D>(vs, vt + hb * D, k0, min(BN, S - k0));
+    stage_rows<T, D>(ks, kt + hq * D, k0, min(BN, S - k0));
+    stage_rows<T, D>(vs, vt + hq * D, k0, min(BN, S - k0));
     __syncthreads();
     float sc[BN];
     float mt = m;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_valu(int S, const T *__restric
 
 // dQ~ (query-stationary): dq_m = scale * sum_{m' <= m} P_mm' (dP_mm' - delta_m) K_m'
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_attn_dq_valu(int S, const T *__restrict__ qt, const T *__restrict__ kt,
+__global__ __launch_bounds__(256) void k_attn_dq_valu(int S, int Sq, const T *__restrict__ qt, const T *__restrict__ kt,
                                                       const T *__restrict__ vt, const float *__restrict__ lse,
                                                       const float *__restrict__ dot, const float *__restrict__ delta,
                                                       float *__restrict__ dqt) {
@@ -109,12 +110,13 @@ __global__ __launch_bounds__(256) void k_attn_dq_valu(int S, const T *__restrict
   const int part = threadIdx.x & 3;
   const int qi = q0 + r;
   const bool active = qi < S;
-  const long long hb = (long long)h * S;
+  const long long hb = (long long)h * S;    // O~, LSE, dO~, gradients: S rows per head
+  const long long hq = (long long)h * Sq;   // gathered Q~, K~, V~: Sq rows per head
   const float scale = 1.f / sqrtf((float)D);
   float qv[DP], gv[DP], acc[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    qv[e] = active ? IO<T>::ld(qt, (hb + qi) * D + part * DP + e) * (scale * kLog2e) : 0.f;
+    qv[e] = active ? IO<T>::ld(qt, (hq + qi) * D + part * DP + e) * (scale * kLog2e) : 0.f;
     gv[e] = active ? dot[(hb + qi) * D + part * DP + e] : 0.f;
     acc[e] = 0.f;
   }
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(256) void k_attn_dq_valu(int S, const T *__restrict
   const int kend = min(S, q0 + BM);
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
-    stage_rows<T, D>(ks, kt + hb * D, k0, min(BN, S - k0));
-    stage_rows<T, D>(vs, vt + hb * D, k0, min(BN, S - k0));
+    stage_rows<T, D>(ks, kt + hq * D, k0, min(BN, S - k0));
+    stage_rows<T, D>(vs, vt + hq * D, k0, min(BN, S - k0));
     __syncthreads();
 #pragma unroll 4
     for (int jj = 0; jj < BN; ++jj) {
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256) void k_attn_dq_valu(int S, const T *__restrict
 // dK~, dV~ (key-stationary): dv_j = sum_{m >= j} P_mj dO~_m ;
 // dk_j = scale * sum_{m >= j} P_mj (dP_mj - delta_m) Q~_m
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_attn_dkv_valu(int S, const T *__restrict__ qt, const T *__restrict__ kt,
+__global__ __launch_bounds__(256) void k_attn_dkv_valu(int S, int Sq, const T *__restrict__ qt, const T *__restrict__ kt,
                                                        const T *__restrict__ vt, const float *__restrict__ lse,
                                                        const float *__restrict__ dot, const float *__restrict__ delta,
                                                        float *__restrict__ dkt, float *__restrict__ dvt) {
@@ -167,18 +169,19 @@ __global__ __launch_bounds__(256) void k_attn_dkv_valu(int S, const T *__restric
   const int part = threadIdx.x & 3;
   const int kj = j0 + r;
   const bool active = kj < S;
-  const long long hb = (long long)h * S;
+  const long long hb = (long long)h * S;    // O~, LSE, dO~, gradients: S rows per head
+  const long long hq = (long long)h * Sq;   // gathered Q~, K~, V~: Sq rows per head
   const float scale = 1.f / sqrtf((float)D);
   float kv[DP], vv[DP], adk[DP], adv[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    kv[e] = active ? IO<T>::ld(kt, (hb + kj) * D + part * DP + e) * (scale * kLog2e) : 0.f;
-    vv[e] = active ? IO<T>::ld(vt, (hb + kj) * D + part * DP + e) : 0.f;
+    kv[e] = active ? IO<T>::ld(kt, (hq + kj) * D + part * DP + e) * (scale * kLog2e) : 0.f;
+    vv[e] = active ? IO<T>::ld(vt, (hq + kj) * D + part * DP + e) : 0.f;
     adk[e] = adv[e] = 0.f;
   }
   for (int m0 = j0; m0 < S; m0 += BN) {
     __syncthreads();
-    stage_rows<T, D>(qs, qt + hb * D, m0, min(BN, S - m0));
+    stage_rows<T, D>(qs, qt + hq * D, m0, min(BN, S - m0));
     for (int idx = threadIdx.x; idx < BN * D; idx += 256) {
       const int rr = idx / D, c = idx % D;
       gs[rr][c] = (m0 + rr < S) ? dot[(hb + m0 + rr) * D + c] : 0.f;
@@ -221,10 +224,10 @@ __global__ __launch_bounds__(256) void k_attn_dkv_valu(int S, const T *__restric
 
 }  // namespace
 
-hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st) {
   dim3 grid((S + BM - 1) / BM, BH);
-#define LH_FWD(T, D) k_attn_fwd_valu<T, D><<<grid, 256, 0, st>>>(S, (const T *)qt, (const T *)kt, (const T *)vt, ot, lse)
+#define LH_FWD(T, D) k_attn_fwd_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, ot, lse)
   if (io == LH_BF16) {
     if (d == 128) LH_FWD(uint16_t, 128);
     else LH_FWD(uint16_t, 64);
@@ -236,16 +239,16 @@ hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, co
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, hipStream_t st) {
   (void)ot;   // delta = rowsum(dO~ * O~) comes from the scatter adjoint
   dim3 grid((S + BM - 1) / BM, BH);
 #define LH_BWD(T, D)                                                                                            \
   do {                                                                                                          \
-    k_attn_dq_valu<T, D><<<grid, 256, 0, st>>>(S, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot, delta, \
+    k_attn_dq_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot, delta, \
                                                dqt);                                                            \
-    k_attn_dkv_valu<T, D><<<grid, 256, 0, st>>>(S, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,       \
+    k_attn_dkv_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,       \
                                                 delta, dkt, dvt);                                               \
   } while (0)
   if (io == LH_BF16) {

@@ -14,8 +14,10 @@
 //   k_compact_gather  tile offset = sum of the earlier tiles' counts; block scan
 //                     inside the tile; writes the slot map (-1 for unselected
 //                     entries), the sorted flat coordinates, and copies the rows
-//                     of Q~, K~, V~ (and V~ transposed, bf16 only) into place.
-#include "lh_internal.h"
+//                     of Q~, K~, V~ into place; in bf16 mode also their
+//                     transposes [d][Sv] with columns in the perm16 order the
+//                     MFMA kernels read (attn_tiles.h).
+#include "attn_tiles.h"
 
 namespace lh {
 
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
   constexpr int RPI = kThreads / CH;   // rows per iteration
   const int j = tid % CH;
   const int rr = tid / CH;
-  const long long hS = (long long)h * s.S;
+  const long long hS = (long long)h * s.Sv;   // gathered rows: head stride Sv
   for (int b0 = 0; b0 < ntot; b0 += 64) {
     for (int r = rr; r < 64 && b0 + r < ntot; r += RPI) {
       const int mm = b0 + r;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
         const int dd = idx / 64;
         const int c = idx % 64;
         if (c < nb) {
-          const long long o = ((long long)h * D + dd) * s.Sv + m0 + b0 + c;
+          const long long o = ((long long)h * D + dd) * s.Sv + tiles::perm16(m0 + b0 + c);
           qtt[o] = stage[0][c][dd];
           ktt[o] = stage[1][c][dd];
           vtt[o] = stage[2][c][dd];
@@ -204,11 +206,21 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
     if (tile == s.ntile - 1) {
       const int pad = s.Sv - s.S;
       for (int idx = tid; idx < D * pad; idx += kThreads) {
-        const long long o = ((long long)h * D + idx / pad) * s.Sv + s.S + idx % pad;
+        const long long o = ((long long)h * D + idx / pad) * s.Sv + tiles::perm16(s.S + idx % pad);
         qtt[o] = 0;
         ktt[o] = 0;
         vtt[o] = 0;
       }
+    }
+  }
+  // zero the padding rows S..Sv-1 of the gathered rows
+  if (tile == s.ntile - 1) {
+    const int pad = s.Sv - s.S;
+    for (int idx = tid; idx < D * pad; idx += kThreads) {
+      const long long o = (hS + s.S) * D + idx;
+      qt[o] = T(0);
+      kt[o] = T(0);
+      vt[o] = T(0);
     }
   }
 }

@@ -18,7 +18,7 @@
 //   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m;
 //   k_pool_bwd     dX_t = sum_l [entry (l, floor(t/p^l)) selected] dX~_slot / p^l
 //                  for X in {Q, K, V} (gather adjoint fused with pool adjoint).
-#include "lh_internal.h"
+#include "attn_tiles.h"
 
 namespace lh {
 
@@ -82,8 +82,8 @@ __device__ __forceinline__ float4 ld4(const void *p, long long off, int dtype) {
 //   delta_m = sum_d dO~[m][d] * O~[m][d]   (the softmax-backward row term)
 // with dO~ as the attention backward will read it (bf16-rounded in bf16 mode).
 // fp32 mode writes dO~ in fp32; bf16 mode writes dO~ in bf16, row-major and
-// transposed ([d][Sv], through an LDS stage so the columns are written
-// coalesced).
+// transposed ([d][Sv], perm16 column order, through an LDS stage so the
+// columns are written coalesced).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__restrict__ dout, int dout_dtype,
                                                      const int *__restrict__ coords, const float *__restrict__ ot,
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   const int r = threadIdx.x >> 2;
   const int part = threadIdx.x & 3;
   const int m = m0 + r;
-  const bool active = m < s.S;
+  const bool active = m < s.S;   // rows S..Sv-1 are written as zeros (bf16 mode)
   float acc[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) acc[e] = 0.f;
@@ -120,6 +120,7 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
     }
   }
   const long long row = ((long long)h * s.S + m) * D + part * DP;
+  const long long rowv = ((long long)h * s.Sv + m) * D + part * DP;   // bf16 dO~: head stride Sv
   float dl = 0.f;
   if constexpr (BF16) {
 #pragma unroll
@@ -141,9 +142,8 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   }
   dl += __shfl_xor(dl, 1);
   dl += __shfl_xor(dl, 2);
-  if (active) {
-    if (part == 0) delta[(long long)h * s.S + m] = dl;
-    if constexpr (BF16) {
+  if constexpr (BF16) {
+    if (m < s.Sv) {
 #pragma unroll
       for (int e = 0; e < DP; e += 8) {
         uint4 w;
@@ -151,9 +151,13 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
         w.y = (unsigned)stage[r][part * DP + e + 2] | ((unsigned)stage[r][part * DP + e + 3] << 16);
         w.z = (unsigned)stage[r][part * DP + e + 4] | ((unsigned)stage[r][part * DP + e + 5] << 16);
         w.w = (unsigned)stage[r][part * DP + e + 6] | ((unsigned)stage[r][part * DP + e + 7] << 16);
-        *reinterpret_cast<uint4 *>(dotb + row + e) = w;
+        *reinterpret_cast<uint4 *>(dotb + rowv + e) = w;
       }
-    } else {
+    }
+  }
+  if (active) {
+    if (part == 0) delta[(long long)h * s.S + m] = dl;
+    if constexpr (!BF16) {
 #pragma unroll
       for (int e = 0; e < DP; e += 4)
         *reinterpret_cast<float4 *>(dot32 + row + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
@@ -165,7 +169,8 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
     const int nb = min(64, s.S - m0);
     for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
       const int dd = idx / 64, c = idx % 64;
-      if (m0 + c < s.Sv) dott[((long long)h * D + dd) * s.Sv + m0 + c] = c < nb ? stage[c][dd] : (uint16_t)0;
+      if (m0 + c < s.Sv)
+        dott[((long long)h * D + dd) * s.Sv + tiles::perm16(m0 + c)] = c < nb ? stage[c][dd] : (uint16_t)0;
     }
   }
 }
@@ -225,7 +230,8 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void
 
 hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
                               float *dot32, uint16_t *dotb, uint16_t *dott, float *delta, hipStream_t st) {
-  dim3 grid((unsigned)((s.S + 63) / 64), s.BH);
+  // bf16 mode also writes the zero padding rows / columns up to Sv (a multiple of 64)
+  dim3 grid((unsigned)(((s.io == LH_BF16 ? s.Sv : s.S) + 63) / 64), s.BH);
   const bool bf = s.io == LH_BF16;
 #define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, dott, delta)
   if (s.d == 128) {

@@ -11,11 +11,11 @@
 #include "lh_internal.h"
 
 namespace lh {
-hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st);
-hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int vstride, const void *qt, const void *kt, const void *vtt,
+hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, int vstride, const void *qt, const void *kt, const void *vtt,
                                 float *ot, float *lse, hipStream_t st);
-hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, const void *qt, const void *kt, const void *vt,
+hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
@@ -109,9 +109,10 @@ void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
   o->flags = take(BH * P);
   o->slot = take(4 * BH * P);
   o->coords = take(4 * BH * S);
-  o->qt = take(es * BH * S * d);
-  o->kt = take(es * BH * S * d);
-  o->vt = take(es * BH * S * d);
+  const size_t Sv = (size_t)s.Sv;
+  o->qt = take(es * BH * Sv * d);
+  o->kt = take(es * BH * Sv * d);
+  o->vt = take(es * BH * Sv * d);
   o->vtt = take(es * BH * (size_t)s.Sv * d);
   o->qtt = take(es * BH * (size_t)s.Sv * d);
   o->ktt = take(es * BH * (size_t)s.Sv * d);
@@ -156,7 +157,7 @@ void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
   };
   const bool bf = s.io == LH_BF16;
   w->dot = take(bf ? 0 : 4 * BH * S * d);
-  w->dotb = take(bf ? 2 * BH * S * d : 0);
+  w->dotb = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
   w->dott = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
   w->delta = take(4 * BH * S);
   w->dqt = take(4 * BH * S * d);
@@ -257,9 +258,9 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   // (iii) causal attention over the sub-sequence
   hipError_t e;
   if (s.io == LH_BF16)
-    e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
+    e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
   else
-    e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
+    e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
   if ((st = hip_check(e, "attention")) != LH_OK) return st;
   // (iv) scatter-back
   if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
@@ -315,7 +316,7 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
     e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
                                  dotb, dott, lse, delta, dqt, dkt, dvt, hs);
   else
-    e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
+    e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
                                  dkt, dvt, hs);
   if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
   // adjoint of the gather and of the pooling
@@ -335,8 +336,8 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *vt, flo
   if (lse && ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be 4-byte aligned");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)((S + 63) & ~63), q, k, vt, o, lse, hs);
-  else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, q, k, vt, o, lse, hs);
+  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)S, (int)((S + 63) & ~63), q, k, vt, o, lse, hs);
+  else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, (int)S, q, k, vt, o, lse, hs);
   return hip_check(e, "attention");
 }
 

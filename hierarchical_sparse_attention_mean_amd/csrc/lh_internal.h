@@ -60,7 +60,7 @@ struct FwdWs {
 // Backward workspace layout.
 struct BwdWs {
   size_t dot;     // fp32 [BH][S][d]  gradient of O~ (LH_F32 mode)
-  size_t dotb;    // bf16 [BH][S][d]  gradient of O~ (LH_BF16 mode)
+  size_t dotb;    // bf16 [BH][Sv][d] gradient of O~ (LH_BF16 mode); rows S..Sv-1 zero
   size_t dott;    // bf16 [BH][d][Sv] gradient of O~, transposed (LH_BF16 mode)
   size_t delta;   // fp32 [BH][S]     rowsum(dO~ * O~)
   size_t dqt;     // fp32 [BH][S][d]

@@ -214,7 +214,8 @@ def saved_view(saved, plan, name):
     io = torch.bfloat16 if plan.io == LH_BF16 else torch.float32
     spec = {
         "scores": (torch.float32, (BH, 2, P)), "flags": (torch.uint8, (BH, P)), "slot": (torch.int32, (BH, P)),
-        "coords": (torch.int32, (BH, S)), "qt": (io, (BH, S, d)), "kt": (io, (BH, S, d)), "vt": (io, (BH, S, d)),
+        "coords": (torch.int32, (BH, S)), "qt": (io, (BH, lay["Sv"], d)), "kt": (io, (BH, lay["Sv"], d)),
+        "vt": (io, (BH, lay["Sv"], d)),
         "vtt": (io, (BH, d, lay["Sv"])), "qtt": (io, (BH, d, lay["Sv"])), "ktt": (io, (BH, d, lay["Sv"])),
         "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
     }[name]

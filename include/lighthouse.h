@@ -66,14 +66,15 @@ typedef struct lh_saved_layout_t {
   size_t flags;    /* uint8 [BH][P]     1 = entry is in the index set I */
   size_t slot;     /* int32 [BH][P]     position in the sub-sequence, -1 if not selected */
   size_t coords;   /* int32 [BH][S]     flat pyramid index of the entry at each slot */
-  size_t qt;       /* io    [BH][S][d]  gathered Q~ (topological order) */
-  size_t kt;       /* io    [BH][S][d]  gathered K~ */
-  size_t vt;       /* io    [BH][S][d]  gathered V~ */
+  size_t qt;       /* io    [BH][Sv][d] gathered Q~ (topological order); rows S..Sv-1 zero */
+  size_t kt;       /* io    [BH][Sv][d] gathered K~; rows S..Sv-1 zero */
+  size_t vt;       /* io    [BH][Sv][d] gathered V~; rows S..Sv-1 zero */
   size_t vtt;      /* io    [BH][d][Sv] V~ transposed, row stride Sv = S rounded up to a multiple
-                            of 64, columns S..Sv-1 zero (operand layout of the bf16 MFMA P.V
-                            product; LH_BF16 only) */
-  size_t qtt;      /* io    [BH][d][Sv] Q~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
-  size_t ktt;      /* io    [BH][d][Sv] K~ transposed (bf16 MFMA backward operand; LH_BF16 only) */
+                            of 64; element m of a row sits at column perm16(m) = m with bits 2
+                            and 3 swapped; columns of m >= S zero (operand layout of the bf16
+                            MFMA kernels; LH_BF16 only) */
+  size_t qtt;      /* io    [BH][d][Sv] Q~ transposed, same layout (LH_BF16 only) */
+  size_t ktt;      /* io    [BH][d][Sv] K~ transposed, same layout (LH_BF16 only) */
   size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
   size_t lse;      /* fp32  [BH][S]     natural-log log-sum-exp of each O~ row's logits */
   size_t total;    /* bytes needed */
@@ -124,8 +125,9 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
  * dense baseline at S = N.
  *   q, k   : [BH][S][d] dtype `io`.
  *   vt     : LH_BF16: V transposed, [BH][d][Sv] with row stride Sv = S rounded up
- *            to a multiple of 64 and columns S..Sv-1 zero (the bf16 MFMA kernel's
- *            operand layout);
+ *            to a multiple of 64, element m of a row at column perm16(m) (m with
+ *            bits 2 and 3 swapped) and the columns of m >= S zero (the bf16 MFMA
+ *            kernel's operand layout);
  *            LH_F32: V itself, [BH][S][d].
  *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
 lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,

@@ -37,7 +37,7 @@ def test_query_matches_closed_form(lh, B, H, N, d, L, p, k, io):
     BH = B * H
     order = ["scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse"]
     need = {"scores": 8 * BH * lay["P"], "flags": BH * lay["P"], "slot": 4 * BH * lay["P"], "coords": 4 * BH * S,
-            "qt": es * BH * S * d, "kt": es * BH * S * d, "vt": es * BH * S * d, "vtt": es * BH * lay["Sv"] * d,
+            "qt": es * BH * lay["Sv"] * d, "kt": es * BH * lay["Sv"] * d, "vt": es * BH * lay["Sv"] * d, "vtt": es * BH * lay["Sv"] * d,
             "qtt": es * BH * lay["Sv"] * d, "ktt": es * BH * lay["Sv"] * d,
             "ot": 4 * BH * S * d, "lse": 4 * BH * S}
     for a, b in zip(order, order[1:] + ["total"]):

@@ -70,8 +70,10 @@ def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True,
         rel = 2.0 ** -8 if dt == "bf16" else 2e-6
         assert np.all(np.abs(got[~base] - ref[~base]) <= rel * np.abs(ref[~base]) + 1e-6), f"{name} pooled rows"
     if dt == "bf16":
+        Sv = g["vtt"].shape[1]
         for tn, n in (("vtt", "vt"), ("qtt", "qt"), ("ktt", "kt")):
             assert np.array_equal(g[tn][:, :S].T, g[n]), f"{tn}: transposed copy differs"
+            assert not np.any(g[tn][:, S:Sv]) and not np.any(g[n + "_pad"]), f"{n}: padding not zero"
     # ---- attention on the GPU's own gathered rows
     if full_attention:
         ot_ref, lse_ref = orc.attend(g["qt"], g["kt"], g["vt"])

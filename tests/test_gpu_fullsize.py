@@ -68,6 +68,7 @@ def _check_full_head(cfg, inp, run, lh, h):
     Sv = run["plan"].layout["Sv"]
     for tn, n in (("vtt", "vt"), ("qtt", "qt"), ("ktt", "kt")):
         assert np.array_equal(g[tn][:, :S].T, g[n]) and not np.any(g[tn][:, S:Sv])
+        assert not np.any(g[n + "_pad"])
     # attention rows on the GPU's gathered rows
     arows = np.unique(np.concatenate([[0, 1, S // 2, S - 1], rng.integers(0, S, 92)]))
     ot_ref, lse_ref = orc.attend_rows(g["qt"], g["kt"], g["vt"], arows)
