@@ -6,8 +6,12 @@
 // contiguous 1 KB block and no registers hold the data in flight.  Since the
 // blocks are contiguous, LDS rows cannot be padded; bank conflicts are avoided
 // instead by XOR-swizzling the 16-byte chunks of each row: logical chunk c of
-// row r is stored at chunk c ^ swz(r), chosen so that 8 consecutive rows put
-// the same logical chunk in 8 different 16-byte bank groups.
+// row r is stored at chunk c ^ swz(r).  The LDS has 64 four-byte banks and
+// serves a 16-byte read for 16 lanes per cycle, and the MFMA operand reads have
+// 16 consecutive lanes on 16 consecutive rows at the same logical chunk, so
+// swz is chosen to put those 16 reads in 16 different 16-byte bank groups: for
+// W-byte rows, row r starts at bank group (r * W / 16) mod 16 and swz adds the
+// remaining spread, swz(r) = (r / (256 / W)) mod (W / 16).
 //
 // MFMA operand reads (v_mfma_f32_32x32x16_bf16): lane (ln, hf) = (lane % 32,
 // lane / 32) reads row ln of a 32-row block, logical chunk 2c + hf, i.e. the 8
@@ -30,10 +34,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // column position of element m in a transposed copy: bits 2 and 3 swapped
 __host__ __device__ __forceinline__ int perm16(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// chunk swizzle for rows of W bytes
+// chunk swizzle for rows of W bytes (W = 64, 128 or 256)
 template <int W>
 __device__ __forceinline__ int swz(int r) {
-  return W >= 128 ? (r & 7) : ((r >> 1) & 3);
+  static_assert(W == 64 || W == 128 || W == 256, "row width");
+  return (r / (256 / W)) & (W / 16 - 1);
 }
 
 // byte offset of (row r, logical 16-byte chunk c) in a tile of W-byte rows

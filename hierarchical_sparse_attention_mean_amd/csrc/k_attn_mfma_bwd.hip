@@ -14,15 +14,16 @@
 //                    dP^T = V~ dO~^T (lane = one query), dS^T in registers, and
 //                    accumulates dQ^T += K~^T dS^T with K~^T from LDS.
 //                    8 wavefronts, 256 queries per work-group.
-//   k_attn_bwd_dkdv  key-stationary: the work-group's 128 K~ and V~ rows sit in
-//                    LDS as B operands; per query tile it forms S = Q~ K~^T and
+//   k_attn_bwd_dkdv  key-stationary: a wavefront holds 32 key rows of K~ and V~
+//                    as B operands; per 32-query tile it forms S = Q~ K~^T and
 //                    dP = dO~ V~^T (lane = one key), and accumulates
 //                    dV^T += dO~^T P and dK^T += Q~^T dS with the transposed
 //                    query-side operands from LDS.  4 wavefronts, 128 keys per
 //                    work-group (the accumulators need the register file of a
 //                    whole SIMD).
-// Both stream their tiles through double-buffered LDS, filled by direct
-// global->LDS loads (attn_tiles.h) while the previous tile is computed.  The
+// Both stream their tiles through LDS filled by direct global->LDS loads
+// (attn_tiles.h) while earlier tiles are computed; dK/dV software-pipelines
+// the S/dP products of tile t+1 with the softmax of tile t (three buffers).  The
 // transposed operands (K~^T, Q~^T, dO~^T; row stride Sv, a multiple of 64,
 // zero padded, columns in perm16 order) are written by the gather and by the
 // scatter adjoint, so every LDS operand is one 16-byte read per lane.  The
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;
-constexpr int kKvBQ = 32;
+constexpr int kKvBQ = 32;   // query rows per tile (a multiple of 32)
 
 template <int D>
 struct DkvTile {
@@ -194,9 +195,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
                                                                  float *__restrict__ dkt, float *__restrict__ dvt) {
   using Tile = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) Tile buf[2];
-  // K~ and V~ rows of this work-group's keys, loaded once (B operands of S and dP)
-  __shared__ __attribute__((aligned(1024))) char kv[2][kKvBK * Tile::WR];
+  // three tiles in flight: t (dV/dK products), t+1 (S/dP products), t+2 (loading)
+  __shared__ __attribute__((aligned(1024))) Tile buf[3];
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
@@ -210,6 +210,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
 
   // query tiles start below S and are 32 rows: they never pass the padded Sv
   // rows.  A padding query has zero Q~ and dO~ rows, so it adds exactly 0.
+  // LSE / delta of the tile go through a register (written to LDS just before
+  // the barrier) so waiting for them never waits for the tile loads as well
   float rl = 0.f;
   auto fill = [&](Tile &t, int q0) {
     tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.q, qh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     tiles::dma_tile<Tile::WT, D, kKvThreads>(t.qt, qth + 2LL * q0, 2LL * Sv, D - 1);
     tiles::dma_tile<Tile::WT, D, kKvThreads>(t.gt, gth + 2LL * q0, 2LL * Sv, D - 1);
     if (tid < 2 * kKvBQ) {
-      const int r = tid & (kKvBQ - 1);
+      const int r = tid % kKvBQ;
       rl = (q0 + r < S) ? (tid < kKvBQ ? lse[hbS + q0 + r] * kLog2e : delta[hbS + q0 + r]) : 0.f;
     }
   };
@@ -226,11 +228,18 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     else if (tid < 2 * kKvBQ) t.dl[tid - kKvBQ] = rl;
   };
 
-  // keys past Sv (last block) read the last padding row, which is zero
-  tiles::dma_tile<Tile::WR, kKvBK, kKvThreads>(kv[0], reinterpret_cast<const char *>(kt + (hbV + j0) * D), Tile::WR,
-                                               Sv - 1 - j0);
-  tiles::dma_tile<Tile::WR, kKvBK, kKvThreads>(kv[1], reinterpret_cast<const char *>(vt + (hbV + j0) * D), Tile::WR,
-                                               Sv - 1 - j0);
+  // K~, V~ rows of this lane's key: B operands of S and dP (keys past Sv read as zero)
+  bf16x8 kf[KC], vf[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    if (kj < Sv) {
+      kf[c] = *reinterpret_cast<const bf16x8 *>(kt + (hbV + kj) * D + 16 * c + 8 * hf);
+      vf[c] = *reinterpret_cast<const bf16x8 *>(vt + (hbV + kj) * D + 16 * c + 8 * hf);
+    } else {
+      kf[c] = (bf16x8){};
+      vf[c] = (bf16x8){};
+    }
+  }
   const float c2 = kLog2e / sqrtf((float)D);
   f32x16 adk[DB], adv[DB];
 #pragma unroll
@@ -238,60 +247,69 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     adk[b] = (f32x16){};
     adv[b] = (f32x16){};
   }
+  // S = Q~ K~^T and dP = dO~ V~^T of one tile (lane = one key, 16 query rows)
+  auto sdp = [&](const Tile &t, f32x16 &sv, f32x16 &dp) {
+    sv = (f32x16){};
+    dp = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(t.q, off), kf[c], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(t.g, off), vf[c], dp, 0, 0, 0);
+    }
+  };
+
+  // Every wavefront updates its accumulators on every tile (a conditional
+  // update would make them branch-merged values that the compiler keeps out of
+  // the accumulator registers); tiles before this wavefront's keys are
+  // diagonal-masked to zero, which costs at most 3 tiles per wavefront.
   const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
   fill(buf[0], j0);
   put_rows(buf[0]);
+  if (nt > 1) {
+    fill(buf[1], j0 + kKvBQ);
+    put_rows(buf[1]);
+  }
   tiles::dma_wait();
   __syncthreads();
+  f32x16 sv, dp;
+  sdp(buf[0], sv, dp);
   for (int t = 0; t < nt; ++t) {
     const int q0 = j0 + t * kKvBQ;
-    if (t + 1 < nt) fill(buf[(t + 1) & 1], q0 + kKvBQ);
-    const Tile &cur = buf[t & 1];
-    // Every wavefront updates its accumulators on every tile (a conditional
-    // update would make them branch-merged values that the compiler keeps out
-    // of the accumulator registers); tiles before this wavefront's keys are
-    // diagonal-masked to zero, which costs at most 3 tiles per wavefront.
-    {
-      f32x16 sv = (f32x16){}, dp = (f32x16){};
+    if (t + 2 < nt) fill(buf[(t + 2) % 3], q0 + 2 * kKvBQ);
+    const Tile &cur = buf[t % 3];
+    // products of the next tile, independent of this tile's softmax below
+    f32x16 sv_n = (f32x16){}, dp_n = (f32x16){};
+    if (t + 1 < nt) sdp(buf[(t + 1) % 3], sv_n, dp_n);
+    const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
+    bf16x8 pf[2], dsf[2];
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
-        const int koff = tiles::tile_off<Tile::WR>(32 * w + ln, 2 * c + hf);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.q, off), tiles::lds_frag(kv[0], koff), sv, 0,
-                                                     0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.g, off), tiles::lds_frag(kv[1], koff), dp, 0,
-                                                     0, 0);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 8 * g4 + 4 * hf;   // tile rows of the 4 values below
+      const float4 l4 = *reinterpret_cast<const float4 *>(&cur.ls[r0]);
+      const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[r0]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g4 + e;   // register of the 32x32 block
+        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv[e]));
+        if (diag && q0 + r0 + e < kj) pj = 0.f;
+        pf[i >> 3][i & 7] = (__bf16)pj;
+        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv4[e]));
       }
-      // phase boundaries: keep each phase's LDS operand reads inside it (bounded live ranges)
-      __builtin_amdgcn_sched_barrier(0);
-      const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 l4 = *reinterpret_cast<const float4 *>(&cur.ls[8 * g4 + 4 * hf]);
-        const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[8 * g4 + 4 * hf]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv[e]));
-          if (diag && q0 + 8 * g4 + 4 * hf + e < kj) pj = 0.f;
-          pf[i >> 3][i & 7] = (__bf16)pj;
-          dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv4[e]));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf);
-          adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.gt, off), pf[c], adv[b], 0, 0, 0);
-          adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.qt, off), dsf[c], adk[b], 0, 0, 0);
-        }
     }
-    if (t + 1 < nt) put_rows(buf[(t + 1) & 1]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf);
+        adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.gt, off), pf[c], adv[b], 0, 0, 0);
+        adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.qt, off), dsf[c], adk[b], 0, 0, 0);
+      }
+    sv = sv_n;
+    dp = dp_n;
+    if (t + 2 < nt) put_rows(buf[(t + 2) % 3]);
     tiles::dma_wait();
     __syncthreads();
   }
