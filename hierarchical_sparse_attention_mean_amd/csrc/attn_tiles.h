@@ -51,26 +51,57 @@ __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int off) {
   return *reinterpret_cast<const bf16x8 *>(tile + off);
 }
 
+// 32-bit LDS address of a pointer into __shared__ memory, the same in every lane
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p);
+}
+
+// One global->LDS load: lane l writes LDS bytes [lds + BYTES l, lds + BYTES (l+1))
+// from gsrc (BYTES = 16 or 4).  The instruction is issued from asm rather than
+// through the compiler's builtin: the compiler cannot tell which LDS buffer such
+// a load writes, so after the builtin it makes the next LDS read of any buffer
+// wait for the load to land -- which would serialize each tile's prefetch with
+// the computation on the tile before it.  Ordering is the kernels' own: a
+// wavefront waits for its loads (s_waitcnt vmcnt) and then meets the others at
+// a barrier before any of them reads the tile.  M0 carries the LDS address; every
+// other use of M0 in these kernels sets it right before use.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int BYTES>
+__device__ __forceinline__ void lds_load(const void *gsrc, unsigned lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Fill an R x W-byte tile: row r comes from gsrc + min(r, rclamp) * gstride.
-// Every wavefront of the NT-thread work-group issues its share of 1 KB blocks.
+// Every wavefront of the NT-thread work-group issues the same number of 1 KB
+// blocks (a fixed trip count, so the fill adds no branches to the caller).
 template <int W, int R, int NT>
 __device__ __forceinline__ void dma_tile(char *lds_tile, const char *gsrc, long long gstride, int rclamp) {
-  constexpr int BLOCKS = R * W / 1024;
-  static_assert(R * W % 1024 == 0, "tile must be whole 1 KB blocks");
+  constexpr int BLOCKS = R * W / 1024, WAVES = NT / 64;
+  static_assert(R * W % 1024 == 0 && BLOCKS % WAVES == 0, "whole 1 KB blocks, as many per wavefront");
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int b = w; b < BLOCKS; b += NT / 64) {
+  for (int i = 0; i < BLOCKS / WAVES; ++i) {
+    const int b = w + i * WAVES;
     const int byte = b * 1024 + 16 * l;
     const int r = byte / W;
     const int pc = (byte % W) / 16;
     const int lc = pc ^ swz<W>(r);
-    const char *src = gsrc + (long long)min(r, rclamp) * gstride + 16 * lc;
-    __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(lds_tile + b * 1024),
-                                     16, 0, 0);
+    lds_load<16>(gsrc + (long long)min(r, rclamp) * gstride + 16 * lc, lds_addr(lds_tile + b * 1024));
   }
 }
 
-// wait for this wavefront's outstanding global loads (the LDS fills included)
+// One dword per lane: lane l of the wavefront writes lds + 4 l from src.
+__device__ __forceinline__ void dma_dword(void *lds, const void *src) { lds_load<4>(src, lds_addr(lds)); }
+
+// wait for this wavefront's outstanding loads (the LDS fills included); a
+// waitcnt written in the source is kept as written by the compiler
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace tiles

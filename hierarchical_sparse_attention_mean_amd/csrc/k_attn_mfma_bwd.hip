@@ -178,8 +178,8 @@ struct DkvTile {
   char g[kKvBQ * WR];
   char qt[D * WT];
   char gt[D * WT];
-  float ls[kKvBQ];
-  float dl[kKvBQ];
+  float ls[kKvBQ];   // LSE (natural log) of the tile's queries
+  float dl[kKvBQ];   // delta of the tile's queries; ls, dl form one 256-byte dword fill
 };
 
 template <int D>
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
                                                                  float *__restrict__ dkt, float *__restrict__ dvt) {
   using Tile = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  // three tiles in flight: t (dV/dK products), t+1 (S/dP products), t+2 (loading)
+  // three tiles in flight: t (softmax, dV/dK products), t+1 (S/dP products), t+2 (loading)
   __shared__ __attribute__((aligned(1024))) Tile buf[3];
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
@@ -208,24 +208,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   const char *qth = reinterpret_cast<const char *>(qtt + (long long)h * D * Sv);
   const char *gth = reinterpret_cast<const char *>(dott + (long long)h * D * Sv);
 
-  // query tiles start below S and are 32 rows: they never pass the padded Sv
-  // rows.  A padding query has zero Q~ and dO~ rows, so it adds exactly 0.
-  // LSE / delta of the tile go through a register (written to LDS just before
-  // the barrier) so waiting for them never waits for the tile loads as well
-  float rl = 0.f;
+  // Query tiles start below S and are 32 rows: they never pass the padded Sv
+  // rows, and a padding query (zero Q~ and dO~ rows) adds exactly 0 whatever
+  // its LSE and delta, which are read clamped to row S-1.  Every wavefront
+  // issues the same 256-byte LSE/delta fill (identical bytes), so the fill has
+  // no branch.
   auto fill = [&](Tile &t, int q0) {
     tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.q, qh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
     tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.g, gh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
     tiles::dma_tile<Tile::WT, D, kKvThreads>(t.qt, qth + 2LL * q0, 2LL * Sv, D - 1);
     tiles::dma_tile<Tile::WT, D, kKvThreads>(t.gt, gth + 2LL * q0, 2LL * Sv, D - 1);
-    if (tid < 2 * kKvBQ) {
-      const int r = tid % kKvBQ;
-      rl = (q0 + r < S) ? (tid < kKvBQ ? lse[hbS + q0 + r] * kLog2e : delta[hbS + q0 + r]) : 0.f;
-    }
-  };
-  auto put_rows = [&](Tile &t) {
-    if (tid < kKvBQ) t.ls[tid] = rl;
-    else if (tid < 2 * kKvBQ) t.dl[tid - kKvBQ] = rl;
+    tiles::dma_dword(t.ls, (hf ? delta : lse) + hbS + min(q0 + ln, S - 1));
   };
 
   // K~, V~ rows of this lane's key: B operands of S and dP (keys past Sv read as zero)
@@ -247,7 +240,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     adk[b] = (f32x16){};
     adv[b] = (f32x16){};
   }
-  // S = Q~ K~^T and dP = dO~ V~^T of one tile (lane = one key, 16 query rows)
+  // S = Q~ K~^T and dP = dO~ V~^T of the first tile (lane = one key, 16 query rows)
   auto sdp = [&](const Tile &t, f32x16 &sv, f32x16 &dp) {
     sv = (f32x16){};
     dp = (f32x16){};
@@ -259,57 +252,87 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     }
   };
 
-  // Every wavefront updates its accumulators on every tile (a conditional
-  // update would make them branch-merged values that the compiler keeps out of
-  // the accumulator registers); tiles before this wavefront's keys are
-  // diagonal-masked to zero, which costs at most 3 tiles per wavefront.
+  // The loop body is one basic block: every wavefront updates its accumulators
+  // on every tile (tiles before its keys are diagonal-masked to zero, at most 3
+  // per wavefront), the fill past the last tile repeats the last tile, and the
+  // S/dP products past the last tile are computed and dropped.  (A conditional
+  // update would also make the accumulators branch-merged values that the
+  // compiler keeps out of the accumulator registers.)
+  //
+  // Issue order within an iteration, fixed with scheduling barriers since one
+  // wavefront per SIMD has no other wavefront to hide its latencies behind:
+  // the fill of tile t+2; all LDS reads of tile t's softmax rows and tile t+1's
+  // S/dP operands; then KC steps, each issuing one S/dP product pair of tile
+  // t+1, the softmax of 16/KC of this lane's values of tile t (VALU work that
+  // runs while the products occupy the matrix core) and two LDS reads of tile
+  // t's dV/dK operands; then the 4 DB dV/dK products of tile t.
+  constexpr int EPS = 16 / KC;   // softmax values per step
+  static_assert(4 * DB == 2 * KC, "two dV/dK operand reads per step");
   const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
+  const int qlast = j0 + (nt - 1) * kKvBQ;       // first query of the last tile
   fill(buf[0], j0);
-  put_rows(buf[0]);
-  if (nt > 1) {
-    fill(buf[1], j0 + kKvBQ);
-    put_rows(buf[1]);
-  }
+  fill(buf[1], min(j0 + kKvBQ, qlast));
   tiles::dma_wait();
   __syncthreads();
   f32x16 sv, dp;
   sdp(buf[0], sv, dp);
   for (int t = 0; t < nt; ++t) {
     const int q0 = j0 + t * kKvBQ;
-    if (t + 2 < nt) fill(buf[(t + 2) % 3], q0 + 2 * kKvBQ);
+    fill(buf[(t + 2) % 3], min(q0 + 2 * kKvBQ, qlast));
     const Tile &cur = buf[t % 3];
-    // products of the next tile, independent of this tile's softmax below
-    f32x16 sv_n = (f32x16){}, dp_n = (f32x16){};
-    if (t + 1 < nt) sdp(buf[(t + 1) % 3], sv_n, dp_n);
-    const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
-    bf16x8 pf[2], dsf[2];
+    const Tile &nxt = buf[(t + 1) % 3];
+    float4 l4[4], d4[4];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = 8 * g4 + 4 * hf;   // tile rows of the 4 values below
-      const float4 l4 = *reinterpret_cast<const float4 *>(&cur.ls[r0]);
-      const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[r0]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      l4[g4] = *reinterpret_cast<const float4 *>(&cur.ls[8 * g4 + 4 * hf]);
+      d4[g4] = *reinterpret_cast<const float4 *>(&cur.dl[8 * g4 + 4 * hf]);
+    }
+    bf16x8 fq[KC], fg[KC];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g4 + e;   // register of the 32x32 block
-        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv[e]));
-        if (diag && q0 + r0 + e < kj) pj = 0.f;
+    for (int c = 0; c < KC; ++c) {
+      const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
+      fq[c] = tiles::lds_frag(nxt.q, off);
+      fg[c] = tiles::lds_frag(nxt.g, off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
+    f32x16 sv_n = (f32x16){}, dp_n = (f32x16){};
+    bf16x8 pf[2], dsf[2];
+    bf16x8 fgt[2][DB], fqt[2][DB];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      sv_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sv_n, 0, 0, 0);
+      dp_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[c], vf[c], dp_n, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int i = EPS * c + u;                  // register of the 32x32 block
+        const int g4 = i >> 2, e = i & 3;
+        const int row = 8 * g4 + 4 * hf + e;        // tile row (query) of the value
+        const float lv = g4 == 0 ? l4[0][e] : g4 == 1 ? l4[1][e] : g4 == 2 ? l4[2][e] : l4[3][e];
+        const float dv = g4 == 0 ? d4[0][e] : g4 == 1 ? d4[1][e] : g4 == 2 ? d4[2][e] : d4[3][e];
+        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv * kLog2e));
+        if (diag && q0 + row < kj) pj = 0.f;
         pf[i >> 3][i & 7] = (__bf16)pj;
-        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv4[e]));
+        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv));
       }
+      // two of the dV/dK operand reads: (cc, b) = c-th pair in (cc, b) order
+      {
+        const int cc = c / DB, b = c % DB;
+        const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * cc + hf);
+        fgt[cc][b] = tiles::lds_frag(cur.gt, off);
+        fqt[cc][b] = tiles::lds_frag(cur.qt, off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf);
-        adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.gt, off), pf[c], adv[b], 0, 0, 0);
-        adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.qt, off), dsf[c], adk[b], 0, 0, 0);
+        adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fgt[c][b], pf[c], adv[b], 0, 0, 0);
+        adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fqt[c][b], dsf[c], adk[b], 0, 0, 0);
       }
     sv = sv_n;
     dp = dp_n;
-    if (t + 2 < nt) put_rows(buf[(t + 2) % 3]);
     tiles::dma_wait();
     __syncthreads();
   }
