@@ -76,7 +76,31 @@ __device__ __forceinline__ void lds_load(const void *gsrc, unsigned lds) {
   else
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
 }
+// The same with a scalar base address and a per-lane 32-bit offset: the base
+// (the same in every lane) stays in scalar registers, so a kernel that keeps
+// the per-lane offsets of its fills in registers spends no vector instructions
+// on fill addresses.
+template <int BYTES>
+__device__ __forceinline__ void lds_load_s(const void *sbase, unsigned voff, unsigned lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Per-lane source offset, for lds_load_s, of 1 KB block b of a tile of W-byte
+// rows whose rows lie gstride bytes apart in global memory (same swizzle as dma_tile).
+template <int W>
+__device__ __forceinline__ unsigned dma_voff(int b, unsigned gstride) {
+  const int byte = b * 1024 + 16 * (int)(threadIdx.x & 63);
+  const int r = byte / W;
+  const int lc = ((byte % W) / 16) ^ swz<W>(r);
+  return (unsigned)r * gstride + 16u * (unsigned)lc;
+}
 
 // Fill an R x W-byte tile: row r comes from gsrc + min(r, rclamp) * gstride.
 // Every wavefront of the NT-thread work-group issues the same number of 1 KB

@@ -63,8 +63,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
                                                                const uint16_t *__restrict__ vt,
                                                                const uint16_t *__restrict__ ktt,
                                                                const uint16_t *__restrict__ dotb,
-                                                               const float *__restrict__ lse,
-                                                               const float *__restrict__ delta,
+                                                               const float *__restrict__ rows,
                                                                float *__restrict__ dqt) {
   using Tile = DqTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
@@ -99,8 +98,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
     }
   }
   const float c2 = kLog2e / sqrtf((float)D);
-  const float lse2 = qi < S ? lse[hbS + qi] * kLog2e : 0.f;
-  const float dl = qi < S ? delta[hbS + qi] : 0.f;
+  // (LSE log2(e), delta) of this lane's query (zero on the padding rows)
+  const float2 rq = qi < Sv ? *reinterpret_cast<const float2 *>(rows + 2 * (hbV + qi)) : make_float2(0.f, 0.f);
+  const float lse2 = rq.x, dl = rq.y;
   f32x16 acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
@@ -168,18 +168,25 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;
-constexpr int kKvBQ = 32;   // query rows per tile (a multiple of 32)
+constexpr int kKvBQ = 32;   // query rows per tile
 
+// One query tile in LDS: Q~ and dO~ rows, their transposes, and the rows'
+// (LSE log2(e), delta) pairs.
 template <int D>
 struct DkvTile {
   static constexpr int WR = 2 * D;       // bytes per Q~ / dO~ row
   static constexpr int WT = 2 * kKvBQ;   // bytes per Q~^T / dO~^T row
-  char q[kKvBQ * WR];
-  char g[kKvBQ * WR];
-  char qt[D * WT];
-  char gt[D * WT];
-  float ls[kKvBQ];   // LSE (natural log) of the tile's queries
-  float dl[kKvBQ];   // delta of the tile's queries; ls, dl form one 256-byte dword fill
+  static constexpr int Q = 0;
+  static constexpr int G = Q + kKvBQ * WR;
+  static constexpr int QT = G + kKvBQ * WR;
+  static constexpr int GT = QT + D * WT;
+  static constexpr int RS = GT + D * WT;
+  static constexpr int BYTES = RS + 8 * kKvBQ;
+};
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
 };
 
 template <int D>
@@ -190,36 +197,70 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
                                                                  const uint16_t *__restrict__ qtt,
                                                                  const uint16_t *__restrict__ dotb,
                                                                  const uint16_t *__restrict__ dott,
-                                                                 const float *__restrict__ lse,
-                                                                 const float *__restrict__ delta,
+                                                                 const float *__restrict__ rows,
                                                                  float *__restrict__ dkt, float *__restrict__ dvt) {
-  using Tile = DkvTile<D>;
+  using T = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  // three tiles in flight: t (softmax, dV/dK products), t+1 (S/dP products), t+2 (loading)
-  __shared__ __attribute__((aligned(1024))) Tile buf[3];
+  constexpr int NC = 4 * DB;   // dV/dK products per tile
+  static_assert(NC == 2 * KC, "one S/dP operand read per dV/dK product");
+  constexpr int EPS = 16 / KC;                                // softmax values per S/dP step
+  constexpr int QBLK = kKvBQ * T::WR / 1024 / kKvWaves;       // 1 KB fill blocks per wavefront: Q~, dO~
+  constexpr int TBLK = D * T::WT / 1024 / kKvWaves;           // ... Q~^T, dO~^T
+  static_assert(QBLK * 1024 * kKvWaves == kKvBQ * T::WR && TBLK * 1024 * kKvWaves == D * T::WT, "fill blocks");
+  // three tiles: t (softmax, dV/dK operands), t+1 (S/dP operands), t+2 (filling)
+  __shared__ __attribute__((aligned(1024))) char lds[3 * T::BYTES];
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int j0 = kb * kKvBK, kw = j0 + 32 * w, kj = kw + ln;
-  const long long hbS = (long long)h * S;    // LSE, delta, dK~, dV~: S rows per head
-  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~: Sv rows per head (rows S..Sv-1 zero)
+  const long long hbS = (long long)h * S;    // dK~, dV~: S rows per head
+  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~, row pairs: Sv rows per head (rows S..Sv-1 zero)
   const char *qh = reinterpret_cast<const char *>(qt + hbV * D);
   const char *gh = reinterpret_cast<const char *>(dotb + hbV * D);
   const char *qth = reinterpret_cast<const char *>(qtt + (long long)h * D * Sv);
   const char *gth = reinterpret_cast<const char *>(dott + (long long)h * D * Sv);
+  const char *rh = reinterpret_cast<const char *>(rows + 2 * hbV);
+  const unsigned lbase = tiles::lds_addr(lds);
 
-  // Query tiles start below S and are 32 rows: they never pass the padded Sv
-  // rows, and a padding query (zero Q~ and dO~ rows) adds exactly 0 whatever
-  // its LSE and delta, which are read clamped to row S-1.  Every wavefront
-  // issues the same 256-byte LSE/delta fill (identical bytes), so the fill has
-  // no branch.
-  auto fill = [&](Tile &t, int q0) {
-    tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.q, qh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
-    tiles::dma_tile<Tile::WR, kKvBQ, kKvThreads>(t.g, gh + (long long)q0 * Tile::WR, Tile::WR, kKvBQ - 1);
-    tiles::dma_tile<Tile::WT, D, kKvThreads>(t.qt, qth + 2LL * q0, 2LL * Sv, D - 1);
-    tiles::dma_tile<Tile::WT, D, kKvThreads>(t.gt, gth + 2LL * q0, 2LL * Sv, D - 1);
-    tiles::dma_dword(t.ls, (hf ? delta : lse) + hbS + min(q0 + ln, S - 1));
+  // Fills: per-lane source offsets are loop invariant; the tile's base address
+  // and the LDS destination are scalars.  Query tiles start below S and are 32
+  // rows, so they never pass the padded Sv rows; a padding query (zero Q~, dO~,
+  // LSE and delta) adds exactly 0.  Every wavefront issues the same 256-byte
+  // fill of the row pairs (identical bytes), so the fill has no branch.
+  unsigned vq[QBLK], vtr[TBLK];
+#pragma unroll
+  for (int i = 0; i < QBLK; ++i) vq[i] = tiles::dma_voff<T::WR>(wu + i * kKvWaves, T::WR);
+#pragma unroll
+  for (int i = 0; i < TBLK; ++i) vtr[i] = tiles::dma_voff<T::WT>(wu + i * kKvWaves, 2u * Sv);
+  const unsigned vrs = 4u * lane;
+  auto fill = [&](int jb, int q0) {
+    const unsigned m = lbase + jb * T::BYTES;
+#pragma unroll
+    for (int i = 0; i < QBLK; ++i) {
+      const unsigned blk = 1024u * (wu + i * kKvWaves);
+      tiles::lds_load_s<16>(qh + (long long)q0 * T::WR, vq[i], m + T::Q + blk);
+      tiles::lds_load_s<16>(gh + (long long)q0 * T::WR, vq[i], m + T::G + blk);
+    }
+#pragma unroll
+    for (int i = 0; i < TBLK; ++i) {
+      const unsigned blk = 1024u * (wu + i * kKvWaves);
+      tiles::lds_load_s<16>(qth + 2LL * q0, vtr[i], m + T::QT + blk);
+      tiles::lds_load_s<16>(gth + 2LL * q0, vtr[i], m + T::GT + blk);
+    }
+    tiles::lds_load_s<4>(rh + 8LL * q0, vrs, m + T::RS);
   };
+
+  // per-lane LDS read offsets (loop invariant): S/dP operands (row ln, chunk
+  // 2c+hf of a row-major tile) and dV/dK operands (row 32b+ln, chunk 2cc+hf of
+  // a transposed tile, c = cc DB + b)
+  int oq[KC], ot[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    oq[c] = tiles::tile_off<T::WR>(ln, 2 * c + hf);
+    ot[c] = tiles::tile_off<T::WT>(32 * (c % DB) + ln, 2 * (c / DB) + hf);
+  }
+  const int ors = T::RS + 32 * hf;   // row pairs 8 g4 + 4 hf + 0..3 at ors + 64 g4
 
   // K~, V~ rows of this lane's key: B operands of S and dP (keys past Sv read as zero)
   bf16x8 kf[KC], vf[KC];
@@ -240,102 +281,105 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     adk[b] = (f32x16){};
     adv[b] = (f32x16){};
   }
-  // S = Q~ K~^T and dP = dO~ V~^T of the first tile (lane = one key, 16 query rows)
-  auto sdp = [&](const Tile &t, f32x16 &sv, f32x16 &dp) {
-    sv = (f32x16){};
-    dp = (f32x16){};
+  // dV/dK operands of the previous tile: P and dS (B operands, from the
+  // softmax) and the dO~^T, Q~^T chunks (A operands, from LDS)
+  bf16x8 pf[2], dsf[2], fgt[KC], fqt[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(t.q, off), kf[c], sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(t.g, off), vf[c], dp, 0, 0, 0);
-    }
+  for (int c = 0; c < 2; ++c) pf[c] = dsf[c] = (bf16x8){};
+#pragma unroll
+  for (int c = 0; c < KC; ++c) fgt[c] = fqt[c] = (bf16x8){};
+  // k-th dV/dK product of the previous tile
+  auto dvdk = [&](int k) {
+    const int c = k >> 1, cc = c / DB, b = c % DB;
+    if (k & 1) adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fqt[c], dsf[cc], adk[b], 0, 0, 0);
+    else adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fgt[c], pf[cc], adv[b], 0, 0, 0);
   };
 
-  // The loop body is one basic block: every wavefront updates its accumulators
-  // on every tile (tiles before its keys are diagonal-masked to zero, at most 3
-  // per wavefront), the fill past the last tile repeats the last tile, and the
-  // S/dP products past the last tile are computed and dropped.  (A conditional
-  // update would also make the accumulators branch-merged values that the
-  // compiler keeps out of the accumulator registers.)
-  //
-  // Issue order within an iteration, fixed with scheduling barriers since one
-  // wavefront per SIMD has no other wavefront to hide its latencies behind:
-  // the fill of tile t+2; all LDS reads of tile t's softmax rows and tile t+1's
-  // S/dP operands; then KC steps, each issuing one S/dP product pair of tile
-  // t+1, the softmax of 16/KC of this lane's values of tile t (VALU work that
-  // runs while the products occupy the matrix core) and two LDS reads of tile
-  // t's dV/dK operands; then the 4 DB dV/dK products of tile t.
-  constexpr int EPS = 16 / KC;   // softmax values per step
-  static_assert(4 * DB == 2 * KC, "two dV/dK operand reads per step");
   const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
   const int qlast = j0 + (nt - 1) * kKvBQ;       // first query of the last tile
-  fill(buf[0], j0);
-  fill(buf[1], min(j0 + kKvBQ, qlast));
+  fill(0, j0);
+  fill(1, min(j0 + kKvBQ, qlast));
   tiles::dma_wait();
   __syncthreads();
-  f32x16 sv, dp;
-  sdp(buf[0], sv, dp);
-  for (int t = 0; t < nt; ++t) {
+  // S = Q~ K~^T, dP = dO~ V~^T of the first tile (lane = one key, 16 query rows)
+  f32x16 sv = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(lds + T::Q, oq[c]), kf[c], sv, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(lds + T::G, oq[c]), vf[c], dp, 0, 0, 0);
+  }
+
+  // Iteration t.  One wavefront per SIMD has no other wavefront to hide its
+  // latencies behind, so the body is one basic block in a fixed issue order:
+  //  1. fill of tile t+2 (into the buffer tile t-1 used);
+  //  2. LDS reads of tile t's row pairs;
+  //  3. the NC dV/dK products of tile t-1 (operands already in registers),
+  //     each followed by one LDS read of tile t+1's S/dP operands -- the
+  //     products cover the read latency;
+  //  4. KC steps, each issuing one S/dP product pair of tile t+1, the softmax
+  //     of EPS of this lane's values of tile t (VALU work that runs while the
+  //     products occupy the matrix core) and two LDS reads of tile t's dV/dK
+  //     operands;
+  //  5. wait for the fill, barrier.
+  // Every wavefront updates its accumulators on every tile; the causal mask is
+  // applied on the first kKvBK/kKvBQ tiles only (on later tiles every query
+  // follows every key of the block); the fill past the last tile repeats the
+  // last tile and the S/dP products past it are dropped.
+  auto iteration = [&](int t, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
     const int q0 = j0 + t * kKvBQ;
-    fill(buf[(t + 2) % 3], min(q0 + 2 * kKvBQ, qlast));
-    const Tile &cur = buf[t % 3];
-    const Tile &nxt = buf[(t + 1) % 3];
-    float4 l4[4], d4[4];
+    const int jc = t % 3, jn = jc == 2 ? 0 : jc + 1, jf = jn == 2 ? 0 : jn + 1;
+    fill(jf, min(q0 + 2 * kKvBQ, qlast));
+    const char *cur = lds + jc * T::BYTES;
+    const char *nxt = lds + jn * T::BYTES;
+    float4 r4[8];   // (LSE log2 e, delta) of rows 8 g4 + 4 hf + {0,1} and {2,3}
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      l4[g4] = *reinterpret_cast<const float4 *>(&cur.ls[8 * g4 + 4 * hf]);
-      d4[g4] = *reinterpret_cast<const float4 *>(&cur.dl[8 * g4 + 4 * hf]);
+      r4[2 * g4] = *reinterpret_cast<const float4 *>(cur + ors + 64 * g4);
+      r4[2 * g4 + 1] = *reinterpret_cast<const float4 *>(cur + ors + 64 * g4 + 16);
     }
     bf16x8 fq[KC], fg[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int off = tiles::tile_off<Tile::WR>(ln, 2 * c + hf);
-      fq[c] = tiles::lds_frag(nxt.q, off);
-      fg[c] = tiles::lds_frag(nxt.g, off);
+    for (int k = 0; k < NC; ++k) {
+      dvdk(k);
+      if (k & 1) fg[k >> 1] = tiles::lds_frag(nxt + T::G, oq[k >> 1]);
+      else fq[k >> 1] = tiles::lds_frag(nxt + T::Q, oq[k >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    const bool diag = q0 < kw + 31;   // causal mask: query >= key (all masked before the keys)
     f32x16 sv_n = (f32x16){}, dp_n = (f32x16){};
-    bf16x8 pf[2], dsf[2];
-    bf16x8 fgt[2][DB], fqt[2][DB];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       sv_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sv_n, 0, 0, 0);
       dp_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[c], vf[c], dp_n, 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < EPS; ++u) {
-        const int i = EPS * c + u;                  // register of the 32x32 block
+        const int i = EPS * c + u;   // register of the 32x32 block: query row 8 g4 + 4 hf + e
         const int g4 = i >> 2, e = i & 3;
-        const int row = 8 * g4 + 4 * hf + e;        // tile row (query) of the value
-        const float lv = g4 == 0 ? l4[0][e] : g4 == 1 ? l4[1][e] : g4 == 2 ? l4[2][e] : l4[3][e];
-        const float dv = g4 == 0 ? d4[0][e] : g4 == 1 ? d4[1][e] : g4 == 2 ? d4[2][e] : d4[3][e];
-        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -lv * kLog2e));
-        if (diag && q0 + row < kj) pj = 0.f;
+        const float4 &rp = r4[2 * g4 + (e >> 1)];
+        const float ls = (e & 1) ? rp.z : rp.x;
+        const float dl = (e & 1) ? rp.w : rp.y;
+        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ls));
+        if constexpr (MASK) {
+          if (q0 + 8 * g4 + 4 * hf + e < kj) pj = 0.f;
+        }
         pf[i >> 3][i & 7] = (__bf16)pj;
-        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dv));
+        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dl));
       }
-      // two of the dV/dK operand reads: (cc, b) = c-th pair in (cc, b) order
-      {
-        const int cc = c / DB, b = c % DB;
-        const int off = tiles::tile_off<Tile::WT>(32 * b + ln, 2 * cc + hf);
-        fgt[cc][b] = tiles::lds_frag(cur.gt, off);
-        fqt[cc][b] = tiles::lds_frag(cur.qt, off);
-      }
+      fgt[c] = tiles::lds_frag(cur + T::GT, ot[c]);
+      fqt[c] = tiles::lds_frag(cur + T::QT, ot[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fgt[c][b], pf[c], adv[b], 0, 0, 0);
-        adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fqt[c][b], dsf[c], adk[b], 0, 0, 0);
-      }
     sv = sv_n;
     dp = dp_n;
     tiles::dma_wait();
     __syncthreads();
-  }
+  };
+  const int nm = min(nt, kKvBK / kKvBQ);
+  for (int t = 0; t < nm; ++t) iteration(t, Flag<true>{});
+  for (int t = nm; t < nt; ++t) iteration(t, Flag<false>{});
+#pragma unroll
+  for (int k = 0; k < NC; ++k) dvdk(k);
+
   if (kj >= S) return;
   const float scale = 1.f / sqrtf((float)D);
   float *krow = dkt + (hbS + kj) * D;
@@ -356,18 +400,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
 
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
                                 const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *lse, const float *delta, float *dqt, float *dkt, float *dvt,
-                                hipStream_t st) {
+                                const float *rows, float *dqt, float *dkt, float *dvt, hipStream_t st) {
   const uint16_t *q = (const uint16_t *)qt, *k = (const uint16_t *)kt, *v = (const uint16_t *)vt;
   const uint16_t *qT = (const uint16_t *)qtt, *kT = (const uint16_t *)ktt;
   const uint16_t *g = (const uint16_t *)dotb, *gT = (const uint16_t *)dott;
   dim3 gq(((S + kDqBM - 1) / kDqBM) * BH), gk(((S + kKvBK - 1) / kKvBK) * BH);
   if (d == 128) {
-    k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
-    k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
+    k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
+    k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
   } else {
-    k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, lse, delta, dqt);
-    k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, lse, delta, dkt, dvt);
+    k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
+    k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
   }
   return hipGetLastError();
 }

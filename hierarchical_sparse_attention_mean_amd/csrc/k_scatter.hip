@@ -81,14 +81,17 @@ __device__ __forceinline__ float4 ld4(const void *p, long long off, int dtype) {
 // columns of dO over the entry's scatter range (t ascending), then
 //   delta_m = sum_d dO~[m][d] * O~[m][d]   (the softmax-backward row term)
 // with dO~ as the attention backward will read it (bf16-rounded in bf16 mode).
-// fp32 mode writes dO~ in fp32; bf16 mode writes dO~ in bf16, row-major and
-// transposed ([d][Sv], perm16 column order, through an LDS stage so the
-// columns are written coalesced).
+// fp32 mode writes dO~ in fp32 and delta; bf16 mode writes dO~ in bf16,
+// row-major and transposed ([d][Sv], perm16 column order, through an LDS stage
+// so the columns are written coalesced), and the per-row pair
+// (LSE log2(e), delta) that the MFMA backward loads with each query tile
+// (zeros on the padding rows S..Sv-1).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__restrict__ dout, int dout_dtype,
                                                      const int *__restrict__ coords, const float *__restrict__ ot,
                                                      float *__restrict__ dot32, uint16_t *__restrict__ dotb,
-                                                     uint16_t *__restrict__ dott, float *__restrict__ delta) {
+                                                     uint16_t *__restrict__ dott, float *__restrict__ delta,
+                                                     const float *__restrict__ lse, float *__restrict__ rows) {
   constexpr int DP = D / 4;
   __shared__ uint16_t stage[BF16 ? 64 : 1][D + 2];
   const int h = blockIdx.y;
@@ -155,9 +158,14 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
       }
     }
   }
+  if constexpr (BF16) {
+    if (part == 0 && m < s.Sv)
+      *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + m)) =
+          active ? make_float2(lse[(long long)h * s.S + m] * 1.4426950408889634f, dl) : make_float2(0.f, 0.f);
+  }
   if (active) {
-    if (part == 0) delta[(long long)h * s.S + m] = dl;
     if constexpr (!BF16) {
+      if (part == 0) delta[(long long)h * s.S + m] = dl;
 #pragma unroll
       for (int e = 0; e < DP; e += 4)
         *reinterpret_cast<float4 *>(dot32 + row + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
@@ -229,11 +237,12 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void
 }
 
 hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
-                              float *dot32, uint16_t *dotb, uint16_t *dott, float *delta, hipStream_t st) {
+                              const float *lse, float *dot32, uint16_t *dotb, uint16_t *dott, float *delta,
+                              float *rows, hipStream_t st) {
   // bf16 mode also writes the zero padding rows / columns up to Sv (a multiple of 64)
   dim3 grid((unsigned)(((s.io == LH_BF16 ? s.Sv : s.S) + 63) / 64), s.BH);
   const bool bf = s.io == LH_BF16;
-#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, dott, delta)
+#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, dott, delta, lse, rows)
   if (s.d == 128) {
     if (bf) LH_SB(128, true);
     else LH_SB(128, false);

@@ -20,8 +20,7 @@ hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void
                                 float *dkt, float *dvt, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
                                 const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *lse, const float *delta, float *dqt, float *dkt, float *dvt,
-                                hipStream_t st);
+                                const float *rows, float *dqt, float *dkt, float *dvt, hipStream_t st);
 }  // namespace lh
 
 namespace {
@@ -159,7 +158,8 @@ void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
   w->dot = take(bf ? 0 : 4 * BH * S * d);
   w->dotb = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
   w->dott = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
-  w->delta = take(4 * BH * S);
+  w->delta = take(bf ? 0 : 4 * BH * S);
+  w->rows = take(bf ? 8 * BH * (size_t)s.Sv : 0);
   w->dqt = take(4 * BH * S * d);
   w->dkt = take(4 * BH * S * d);
   w->dvt = take(4 * BH * S * d);
@@ -299,6 +299,7 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   uint16_t *dotb = reinterpret_cast<uint16_t *>(wb + bw.dotb);
   uint16_t *dott = reinterpret_cast<uint16_t *>(wb + bw.dott);
   float *delta = reinterpret_cast<float *>(wb + bw.delta);
+  float *rows = reinterpret_cast<float *>(wb + bw.rows);
   float *dqt = reinterpret_cast<float *>(wb + bw.dqt);
   float *dkt = reinterpret_cast<float *>(wb + bw.dkt);
   float *dvt = reinterpret_cast<float *>(wb + bw.dvt);
@@ -307,14 +308,14 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   (void)v;
   (void)slot;
   // adjoint of the scatter: dO~ (and delta = rowsum(dO~ * O~))
-  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, dot, dotb, dott, delta, hs),
+  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, dott, delta, rows, hs),
                       "scatter_bwd")) != LH_OK)
     return st;
   // adjoint of the sub-sequence attention
   hipError_t e;
   if (s.io == LH_BF16)
     e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
-                                 dotb, dott, lse, delta, dqt, dkt, dvt, hs);
+                                 dotb, dott, rows, dqt, dkt, dvt, hs);
   else
     e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
                                  dkt, dvt, hs);
