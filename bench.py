@@ -9,18 +9,24 @@ p=4, k=4,096 (S=65,536).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--dense]
 
 Prints one JSON line (rank 0).  Besides the contract fields it carries:
-  roofline      dominant kernel (the sub-sequence attention), algorithmic FLOPs
-                per launch / its mean launch time from HIP events on its stream
+  roofline      the dominant kernel of the step (by time): its algorithmic FLOPs
+                per launch / its mean launch time, from the library's stage
+                timing (HIP events recorded around each launch on the stream it
+                runs on, over the timed steps); `traffic` is the kernel's HBM
+                bytes per launch from hardware counters (profiles/), or null
+                when the kernel's sources changed since the counters were taken
   cpu_baseline  the fp64 oracle on one head of the same workload (fwd + bwd),
                 on this host's cores, scaled to the layer's tokens/s
-  extra         forward-only time, attention fwd/bwd kernel times, and (with
-                --dense) the dense causal attention kernel at S = N
+  extra         per-stage times, forward-only time, and (with --dense) the dense
+                causal attention kernel at S = N
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,10 +42,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attention_flops(S: int, d: int, BH: int) -> float:
-    """Algorithmic FLOPs of causal attention over S rows: Q.K^T and P.V over
-    the S^2/2 causal pairs, 2 FLOPs per multiply-add."""
-    return 2.0 * 2.0 * (S * S / 2.0) * d * BH
+def attention_flops(S: int, d: int, BH: int, products: int = 2) -> float:
+    """Algorithmic FLOPs of causal attention over S rows: `products` d-long
+    multiply-add contractions per causal (query, key) pair, S (S+1) / 2 pairs
+    per head, 2 FLOPs per multiply-add.  Forward: Q.K^T and P.V (2); dQ~:
+    S, dP, dS.K (3); dK~/dV~: S, dP, P^T.dO, dS^T.Q (4)."""
+    return 2.0 * products * (S * (S + 1) / 2.0) * d * BH
+
+
+# stage -> (matmul products per causal pair, kernel sources) for the MFMA stages
+ATTN_STAGES = {
+    "attn_fwd": (2, ["k_attn_mfma.hip", "attn_tiles.h"]),
+    "attn_bwd_dq": (3, ["k_attn_mfma_bwd.hip", "attn_tiles.h"]),
+    "attn_bwd_dkdv": (4, ["k_attn_mfma_bwd.hip", "attn_tiles.h"]),
+}
+
+
+def sources_sha256(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "hierarchical_sparse_attention_mean_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(stage: str, config: str):
+    """HBM bytes per launch of a stage's kernel from its committed counter
+    summary (profiles/<stage>_<config>_pmc.md), or None if there is none or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{config}_pmc.md")
+    if stage not in ATTN_STAGES or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = {k: re.search(rf"^{k}:\s*(\S+)", text, re.M) for k in ("source_sha256", "fetch_bytes_per_launch",
+                                                               "write_bytes_per_launch")}
+    if not all(m.values()) or m["source_sha256"].group(1) != sources_sha256(ATTN_STAGES[stage][1]):
+        return None
+    return float(m["fetch_bytes_per_launch"].group(1)) + float(m["write_bytes_per_launch"].group(1))
 
 
 def cpu_baseline(cfg: dict) -> dict:
@@ -77,6 +116,9 @@ def main() -> int:
     ap.add_argument("--config", default="512k")
     ap.add_argument("--dense", action="store_true", help="also time dense causal attention at S = N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the timed steps (a known-size "
+                         "reference dispatch for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (heads or sequence shards "
@@ -135,14 +177,29 @@ def main() -> int:
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy: {args.copy_mib} MiB read, {args.copy_mib} MiB written")
+        del src, dst
     torch.cuda.synchronize()
+    lh.lh_timing_begin()   # events around each stage's launches, on their stream
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    st, stages = lh.lh_timing_end()
+    if st:
+        raise lh.LighthouseError(st, "lh_timing_end")
     ms = (t1 - t0) * 1e3 / args.steps
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step")
+    stage_ms = {n: {"ms_per_step": t / args.steps, "ms_per_launch": t / c if c else None, "launches_per_step": c / args.steps}
+                for n, (t, c) in stages.items()}
+    for n, rec in stage_ms.items():
+        log(f"[bench]   {n:14s} {rec['ms_per_step']:8.3f} ms/step")
 
     # forward alone
     torch.cuda.synchronize()
@@ -153,30 +210,21 @@ def main() -> int:
     ms_fwd = (time.perf_counter() - t0) * 1e3 / args.steps
     log(f"[bench] forward only: {ms_fwd:.3f} ms")
 
-    # dominant kernel: the sub-sequence attention, launched exactly as inside
-    # lh_forward (same kernel, grid and operands), timed with HIP events on the
-    # stream it runs on
-    qt = lh.saved_view(saved, plan, "qt")
-    kt = lh.saved_view(saved, plan, "kt")
-    vop = lh.saved_view(saved, plan, "vtt" if io == torch.bfloat16 else "vt")
-    ot = torch.empty((BH, S, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((BH, S), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        st = lh.lh_attention_forward(qt, kt, vop, ot, lse, BH, S, d, io)
-        b.record(stream)
-        if st:
-            raise lh.LighthouseError(st, "lh_attention_forward")
-    torch.cuda.synchronize()
-    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    flops = attention_flops(S, d, BH)
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    log(f"[bench] attention forward kernel: {attn_ms:.3f} ms, {achieved:.1f} TFLOP/s")
+    # dominant kernel: the MFMA attention stage with the most time per step
+    dom = max(ATTN_STAGES, key=lambda n: stage_ms[n]["ms_per_step"])
+    dom_ms = stage_ms[dom]["ms_per_launch"]
+    dom_flops = attention_flops(S, d, BH, ATTN_STAGES[dom][0])
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = counter_traffic(dom, args.config)
+    log(f"[bench] dominant kernel {dom}: {dom_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s")
+    for n in ATTN_STAGES:
+        rec = stage_ms[n]
+        if rec["ms_per_launch"]:
+            rec["tflops"] = attention_flops(S, d, BH, ATTN_STAGES[n][0]) / (rec["ms_per_launch"] * 1e-3) / 1e12
 
-    extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "attn_fwd_kernel_ms": attn_ms,
-             "attn_fwd_flops": flops, "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
+    extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "stages": stage_ms,
+             "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
+    stream = torch.cuda.current_stream()
     if args.dense:
         if io == torch.bfloat16:   # V^T, columns in the kernel's order (bits 2 and 3 of the index swapped)
             col = torch.arange(N, device=dev)
@@ -218,9 +266,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"Lighthouse layer fwd+bwd, {args.config}: B={B} H={H} d={d} N={N} L={L} p={p} "
                                f"k={k} (S={S})", "B": B, "H": H, "d": d, "N": N, "L": L, "p": p, "k": k, "S": S},
-        "roofline": {"bound": "mfma", "kernel": "sub-sequence causal attention forward", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "flops_per_launch": dom_flops, "ms_per_launch": dom_ms},
         "cpu_baseline": cpu,
         "extra": extra,
     }

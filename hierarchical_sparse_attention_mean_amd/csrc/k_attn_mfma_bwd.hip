@@ -400,17 +400,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
 
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
                                 const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *rows, float *dqt, float *dkt, float *dvt, hipStream_t st) {
+                                const float *rows, float *dqt, float *dkt, float *dvt, int part, hipStream_t st) {
   const uint16_t *q = (const uint16_t *)qt, *k = (const uint16_t *)kt, *v = (const uint16_t *)vt;
   const uint16_t *qT = (const uint16_t *)qtt, *kT = (const uint16_t *)ktt;
   const uint16_t *g = (const uint16_t *)dotb, *gT = (const uint16_t *)dott;
   dim3 gq(((S + kDqBM - 1) / kDqBM) * BH), gk(((S + kKvBK - 1) / kKvBK) * BH);
-  if (d == 128) {
-    k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
-    k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
-  } else {
-    k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
-    k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
+  if (part == 0) {   // dQ~
+    if (d == 128) k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
+    else k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
+  } else {           // dK~, dV~
+    if (d == 128) k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
+    else k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
   }
   return hipGetLastError();
 }

@@ -241,15 +241,17 @@ hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void
 
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
-                                float *dkt, float *dvt, hipStream_t st) {
+                                float *dkt, float *dvt, int part, hipStream_t st) {
   (void)ot;   // delta = rowsum(dO~ * O~) comes from the scatter adjoint
   dim3 grid((S + BM - 1) / BM, BH);
 #define LH_BWD(T, D)                                                                                            \
   do {                                                                                                          \
-    k_attn_dq_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot, delta, \
-                                               dqt);                                                            \
-    k_attn_dkv_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,       \
-                                                delta, dkt, dvt);                                               \
+    if (part == 0)                                                                                              \
+      k_attn_dq_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,     \
+                                                 delta, dqt);                                                   \
+    else                                                                                                        \
+      k_attn_dkv_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,    \
+                                                  delta, dkt, dvt);                                             \
   } while (0)
   if (io == LH_BF16) {
     if (d == 128) LH_BWD(uint16_t, 128);

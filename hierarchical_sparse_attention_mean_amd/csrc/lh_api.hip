@@ -1,12 +1,15 @@
 // C ABI of liblighthouse.so: argument validation, buffer layouts and the launch
 // sequence of the Lighthouse layer ("Long Context Pre-Training with Lighthouse
 // Attention", Sec. 3.2-3.6).  Nothing here allocates, frees or synchronises;
-// every call only enqueues kernels on the caller's stream.
+// every call only enqueues kernels on the caller's stream -- except while the
+// calling thread has stage timing switched on (lh_timing_begin / lh_timing_end),
+// when each stage's launches are bracketed by a pair of HIP events.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "lh_internal.h"
 
@@ -17,15 +20,67 @@ hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, int vstride, const
                                 float *ot, float *lse, hipStream_t st);
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
-                                float *dkt, float *dvt, hipStream_t st);
+                                float *dkt, float *dvt, int part, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
                                 const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *rows, float *dqt, float *dkt, float *dvt, hipStream_t st);
+                                const float *rows, float *dqt, float *dkt, float *dvt, int part, hipStream_t st);
 }  // namespace lh
 
 namespace {
 
 thread_local std::string g_err;
+
+// Stage timing (per host thread, off unless lh_timing_begin was called).
+struct TimedSpan {
+  int stage;
+  hipEvent_t start, stop;
+};
+thread_local bool t_timing = false;
+thread_local std::vector<TimedSpan> t_spans;
+
+void timing_clear() {
+  for (const TimedSpan &sp : t_spans) {
+    (void)hipEventDestroy(sp.start);
+    (void)hipEventDestroy(sp.stop);
+  }
+  t_spans.clear();
+}
+
+// Brackets the launches of one stage with events on the stage's stream while
+// timing is on; does nothing otherwise.  An event that cannot be created or
+// recorded drops that span from the timing (the launches are unaffected).
+class Span {
+ public:
+  Span(int stage, hipStream_t s) : stage_(stage), s_(s) {
+    if (!t_timing) return;
+    if (hipEventCreate(&start_) != hipSuccess) start_ = nullptr;
+    else if (hipEventRecord(start_, s_) != hipSuccess) {
+      (void)hipEventDestroy(start_);
+      start_ = nullptr;
+    }
+  }
+  ~Span() {
+    if (!start_) return;
+    hipEvent_t stop;
+    if (hipEventCreate(&stop) != hipSuccess) {
+      (void)hipEventDestroy(start_);
+      return;
+    }
+    if (hipEventRecord(stop, s_) != hipSuccess) {
+      (void)hipEventDestroy(start_);
+      (void)hipEventDestroy(stop);
+      return;
+    }
+    t_spans.push_back({stage_, start_, stop});
+  }
+  Span(const Span &) = delete;
+  Span &operator=(const Span &) = delete;
+
+ private:
+  int stage_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr;
+};
 
 lh_status fail(lh_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 lh_status fail(lh_status st, const char *fmt, ...) {
@@ -245,25 +300,43 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   float *lse = reinterpret_cast<float *>(sv + sl.lse);
 
   // (ii) top-k state (umin = ~0, the rest 0) and histogram cleared by a kernel
-  if ((st = hip_check(lh::launch_topk_init(s, ws, fw, hs), "topk_init")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_TOPK, hs);
+    if ((st = hip_check(lh::launch_topk_init(s, ws, fw, hs), "topk_init")) != LH_OK) return st;
+  }
   // (i)+(ii) pyramid and scores in one pass over Q, K, V
-  if ((st = hip_check(lh::launch_pool_score(s, q, k, v, ws, fw, scores, hs), "pool_score")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_POOL_SCORE, hs);
+    if ((st = hip_check(lh::launch_pool_score(s, q, k, v, ws, fw, scores, hs), "pool_score")) != LH_OK) return st;
+  }
   // (ii) selection
-  if ((st = hip_check(lh::launch_topk(s, ws, fw, flags, hs), "topk")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_TOPK, hs);
+    if ((st = hip_check(lh::launch_topk(s, ws, fw, flags, hs), "topk")) != LH_OK) return st;
+  }
   // (iii) topological compaction + gather
-  if ((st = hip_check(lh::launch_compact_gather(s, q, k, v, ws, fw, flags, slot, coords, sv + sl.qt, sv + sl.kt,
-                                                sv + sl.vt, sv + sl.vtt, sv + sl.qtt, sv + sl.ktt, hs),
-                      "compact_gather")) != LH_OK)
-    return st;
+  {
+    Span sp(LH_STAGE_GATHER, hs);
+    if ((st = hip_check(lh::launch_compact_gather(s, q, k, v, ws, fw, flags, slot, coords, sv + sl.qt, sv + sl.kt,
+                                                  sv + sl.vt, sv + sl.vtt, sv + sl.qtt, sv + sl.ktt, hs),
+                        "compact_gather")) != LH_OK)
+      return st;
+  }
   // (iii) causal attention over the sub-sequence
-  hipError_t e;
-  if (s.io == LH_BF16)
-    e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
-  else
-    e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
-  if ((st = hip_check(e, "attention")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_ATTN_FWD, hs);
+    hipError_t e;
+    if (s.io == LH_BF16)
+      e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
+    else
+      e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
+    if ((st = hip_check(e, "attention")) != LH_OK) return st;
+  }
   // (iv) scatter-back
-  if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_SCATTER, hs);
+    if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
+  }
   return LH_OK;
 }
 
@@ -308,21 +381,31 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   (void)v;
   (void)slot;
   // adjoint of the scatter: dO~ (and delta = rowsum(dO~ * O~))
-  if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, dott, delta, rows, hs),
-                      "scatter_bwd")) != LH_OK)
-    return st;
-  // adjoint of the sub-sequence attention
-  hipError_t e;
-  if (s.io == LH_BF16)
-    e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
-                                 dotb, dott, rows, dqt, dkt, dvt, hs);
-  else
-    e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta, dqt,
-                                 dkt, dvt, hs);
-  if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  {
+    Span sp(LH_STAGE_SCATTER_BWD, hs);
+    if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, dott, delta, rows, hs),
+                        "scatter_bwd")) != LH_OK)
+      return st;
+  }
+  // adjoint of the sub-sequence attention: dQ~, then dK~ and dV~
+  for (int part = 0; part < 2; ++part) {
+    Span sp(part == 0 ? LH_STAGE_ATTN_BWD_DQ : LH_STAGE_ATTN_BWD_DKDV, hs);
+    hipError_t e;
+    if (s.io == LH_BF16)
+      e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
+                                   dotb, dott, rows, dqt, dkt, dvt, part, hs);
+    else
+      e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta,
+                                   dqt, dkt, dvt, part, hs);
+    if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  }
   // adjoint of the gather and of the pooling
-  if ((st = hip_check(lh::launch_pool_bwd(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype, hs), "pool_bwd")) != LH_OK)
-    return st;
+  {
+    Span sp(LH_STAGE_POOL_BWD, hs);
+    if ((st = hip_check(lh::launch_pool_bwd(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype, hs), "pool_bwd")) !=
+        LH_OK)
+      return st;
+  }
   return LH_OK;
 }
 
@@ -340,6 +423,52 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *vt, flo
   if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)S, (int)((S + 63) & ~63), q, k, vt, o, lse, hs);
   else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, (int)S, q, k, vt, o, lse, hs);
   return hip_check(e, "attention");
+}
+
+const char *lh_stage_name(int stage) {
+  switch (stage) {
+    case LH_STAGE_POOL_SCORE: return "pool_score";
+    case LH_STAGE_TOPK: return "topk";
+    case LH_STAGE_GATHER: return "gather";
+    case LH_STAGE_ATTN_FWD: return "attn_fwd";
+    case LH_STAGE_SCATTER: return "scatter";
+    case LH_STAGE_SCATTER_BWD: return "scatter_bwd";
+    case LH_STAGE_ATTN_BWD_DQ: return "attn_bwd_dq";
+    case LH_STAGE_ATTN_BWD_DKDV: return "attn_bwd_dkdv";
+    case LH_STAGE_POOL_BWD: return "pool_bwd";
+    default: return "unknown";
+  }
+}
+
+lh_status lh_timing_begin(void) {
+  timing_clear();
+  t_timing = true;
+  return LH_OK;
+}
+
+lh_status lh_timing_end(double *ms, int *spans, int n) {
+  if (n < 0 || (n > 0 && (!ms || !spans))) return fail(LH_EINVAL, "ms and spans must hold n >= 0 entries");
+  t_timing = false;
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    spans[i] = 0;
+  }
+  lh_status st = LH_OK;
+  for (const TimedSpan &sp : t_spans) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(sp.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, sp.start, sp.stop);
+    if (e != hipSuccess) {
+      if (st == LH_OK) st = fail(LH_EHIP, "stage timing: %s", hipGetErrorString(e));
+      continue;
+    }
+    if (sp.stage < n) {
+      ms[sp.stage] += t;
+      spans[sp.stage] += 1;
+    }
+  }
+  timing_clear();
+  return st;
 }
 
 }  // extern "C"

@@ -60,6 +60,13 @@ _lib.lh_status_string.argtypes = [_i]
 _lib.lh_status_string.restype = ctypes.c_char_p
 _lib.lh_last_error.argtypes = []
 _lib.lh_last_error.restype = ctypes.c_char_p
+_lib.lh_stage_name.argtypes = [_i]
+_lib.lh_stage_name.restype = ctypes.c_char_p
+_lib.lh_timing_begin.argtypes = []
+_lib.lh_timing_begin.restype = _i
+_lib.lh_timing_end.argtypes = [_P(ctypes.c_double), _P(_i), _i]
+_lib.lh_timing_end.restype = _i
+STAGE_COUNT = 9   # LH_STAGE_COUNT
 
 
 def library():
@@ -110,6 +117,22 @@ def lh_status_string(status: int) -> str:
 
 def lh_last_error() -> str:
     return _lib.lh_last_error().decode()
+
+
+def lh_stage_name(stage: int) -> str:
+    return _lib.lh_stage_name(stage).decode()
+
+
+def lh_timing_begin() -> int:
+    return _lib.lh_timing_begin()
+
+
+def lh_timing_end():
+    """Returns (status, {stage name: (summed ms, spans)}) for every stage."""
+    ms = (ctypes.c_double * STAGE_COUNT)()
+    spans = (_i * STAGE_COUNT)()
+    st = _lib.lh_timing_end(ms, spans, STAGE_COUNT)
+    return st, {lh_stage_name(i): (ms[i], spans[i]) for i in range(STAGE_COUNT)}
 
 
 def lh_query(B, H, N, d, L, p, topk, io):

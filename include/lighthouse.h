@@ -33,9 +33,9 @@
  *  - Supported: d in {64, 128}; io dtype LH_F32 or LH_BF16 (bf16 storage, fp32
  *    arithmetic, bf16 MFMA for the attention); L >= 1; p >= 2; topk >= 0.
  *    topk larger than the candidates selects everything (S = |P|).
- *  - No global mutable state except the thread-local error text: calls are
- *    re-entrant; concurrent calls on different streams must use distinct
- *    buffers.
+ *  - No global mutable state except the thread-local error text and the
+ *    thread-local stage timing switch (lh_timing_begin): calls are re-entrant;
+ *    concurrent calls on different streams must use distinct buffers.
  */
 #ifndef LIGHTHOUSE_H
 #define LIGHTHOUSE_H
@@ -132,6 +132,35 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
  *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
 lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,
                                int BH, int64_t S, int d, lh_dtype io, void *stream);
+
+/* Stages of lh_forward / lh_backward, for stage timing. */
+typedef enum {
+  LH_STAGE_POOL_SCORE = 0,   /* (i)+(ii): pyramid and scores, one pass over Q, K, V          */
+  LH_STAGE_TOPK = 1,         /* (ii): joint top-B selection (state clear + 3 passes)          */
+  LH_STAGE_GATHER = 2,       /* (iii): topological compaction and gather                      */
+  LH_STAGE_ATTN_FWD = 3,     /* (iii): causal attention over the sub-sequence (Eq. 9)         */
+  LH_STAGE_SCATTER = 4,      /* (iv): scatter to the base positions                           */
+  LH_STAGE_SCATTER_BWD = 5,  /* adjoint of (iv): dO~ and the softmax row terms               */
+  LH_STAGE_ATTN_BWD_DQ = 6,  /* adjoint of Eq. 9: dQ~                                         */
+  LH_STAGE_ATTN_BWD_DKDV = 7,/* adjoint of Eq. 9: dK~, dV~                                    */
+  LH_STAGE_POOL_BWD = 8,     /* adjoint of the gather and of the pooling: dQ, dK, dV          */
+  LH_STAGE_COUNT = 9
+} lh_stage;
+
+/* Host-only.  Short name of a stage ("attn_bwd_dkdv", ...; static storage). */
+const char *lh_stage_name(int stage);
+
+/* Host-only.  Stage timing, for benchmarks (not part of the compute path).
+ * lh_timing_begin switches timing on for the calling host thread and drops
+ * any earlier records.  While it is on, lh_forward and lh_backward bracket the
+ * kernel launches of each stage with a pair of HIP events recorded on the
+ * call's stream -- the only time the library creates anything.
+ * lh_timing_end switches it off, waits for the recorded events, and writes for
+ * each stage s < n the summed elapsed milliseconds ms[s] and the number of
+ * bracketed spans spans[s]; stages >= n are dropped.  It releases the events.
+ * Returns LH_EHIP (after filling what it could) if an event fails. */
+lh_status lh_timing_begin(void);
+lh_status lh_timing_end(double *ms, int *spans, int n);
 
 /* Text of a status code (static storage). */
 const char *lh_status_string(lh_status s);

@@ -101,3 +101,20 @@ def test_forward_validation_before_launch(lh):
                           "f32", fake, bws) == 1
     # dense attention: unsupported d
     assert lh.lh_attention_forward(fake, fake, fake, fake, None, 1, 128, 80, "bf16") == 3
+
+
+def test_stage_timing_host_side(lh):
+    """Stage names and enum size match the header; timing with no calls in
+    between records nothing; bad output arrays are rejected.  (No GPU work.)"""
+    import re
+    hdr = open(lh.HEADER).read()
+    names = [lh.lh_stage_name(i) for i in range(lh.STAGE_COUNT)]
+    assert names == ["pool_score", "topk", "gather", "attn_fwd", "scatter", "scatter_bwd", "attn_bwd_dq",
+                     "attn_bwd_dkdv", "pool_bwd"]
+    assert lh.lh_stage_name(lh.STAGE_COUNT) == "unknown"
+    assert int(re.search(r"LH_STAGE_COUNT\s*=\s*(\d+)", hdr).group(1)) == lh.STAGE_COUNT
+    assert lh.lh_timing_begin() == 0
+    st, stages = lh.lh_timing_end()
+    assert st == 0 and all(ms == 0.0 and s == 0 for ms, s in stages.values())
+    assert lh.library().lh_timing_end(None, None, 3) == 1
+    assert lh.library().lh_timing_end(None, None, 0) == 0

@@ -105,3 +105,32 @@ def test_backward_properties_scale_and_determinism(lh):
         assert torch.isfinite(a).all()
         assert torch.equal(a, c)
         assert torch.equal(2 * a, b)
+
+
+def test_stage_timing_leaves_results_unchanged(lh):
+    """Stage timing (events around each stage's launches) changes no output
+    bit, and records every stage of the forward and the backward."""
+    import torch
+    cfg = synth.config("bwd8k", N=65536, H=2)
+    inp = synth.make_inputs(cfg, with_do=True)
+    run = run_forward(lh, cfg, inp)
+    dout = to_dev(inp["do"], cfg["dtype"])
+    g1 = lh.backward(run["q"], run["k"], run["v"], dout, run["saved"], run["plan"], grad_dtype=torch.float32)
+    o1 = run["o"].clone()
+    torch.cuda.synchronize()
+    assert lh.lh_timing_begin() == 0
+    run2 = run_forward(lh, cfg, inp)
+    g2 = lh.backward(run2["q"], run2["k"], run2["v"], dout, run2["saved"], run2["plan"], grad_dtype=torch.float32)
+    st, stages = lh.lh_timing_end()
+    assert st == 0, lh.lh_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, run2["o"])
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for name, (ms, spans) in stages.items():
+        say(f"  stage {name}: {spans} spans, {ms:.3f} ms")
+        assert spans == (2 if name == "topk" else 1) and ms > 0, name
+    # switched off again: a further call records nothing
+    lh.lh_timing_begin()
+    st, stages = lh.lh_timing_end()
+    assert st == 0 and all(s == 0 for _, s in stages.values())
