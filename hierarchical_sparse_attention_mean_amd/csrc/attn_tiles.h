@@ -128,5 +128,28 @@ __device__ __forceinline__ void dma_dword(void *lds, const void *src) { lds_load
 // waitcnt written in the source is kept as written by the compiler
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N of this wavefront's global loads are outstanding --
+// loads complete in issue order, so every fill issued before the last N loads
+// has landed -- and all its LDS reads have returned, then meet the other
+// wavefronts of the work-group at a barrier.  One asm statement, so the
+// compiler moves no memory access across it and adds no wait of its own (the
+// fence of __syncthreads would wait for every outstanding load).  Used with
+// fills issued two or more tiles ahead: N = the loads of the fills still
+// allowed in flight.
+template <int N>
+__device__ __forceinline__ void wait_fills_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The same, but leaving this wavefront's last M LDS reads in flight (LDS reads
+// complete in issue order): for reads already issued from a tile that the
+// fills after the barrier do not overwrite.
+template <int N, int M>
+__device__ __forceinline__ void wait_fills_barrier_keep() {
+  static_assert(N >= 0 && N < 64 && M >= 0 && M < 16, "vmcnt / lgkmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(N), "n"(M) : "memory");
+}
+
 }  // namespace tiles
 }  // namespace lh

@@ -169,6 +169,7 @@ constexpr int kKvWaves = 4;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvBK = 32 * kKvWaves;
 constexpr int kKvBQ = 32;   // query rows per tile
+constexpr int kKvBufs = 4;  // tiles in LDS
 
 // One query tile in LDS: Q~ and dO~ rows, their transposes, and the rows'
 // (LSE log2(e), delta) pairs.
@@ -207,8 +208,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   constexpr int QBLK = kKvBQ * T::WR / 1024 / kKvWaves;       // 1 KB fill blocks per wavefront: Q~, dO~
   constexpr int TBLK = D * T::WT / 1024 / kKvWaves;           // ... Q~^T, dO~^T
   static_assert(QBLK * 1024 * kKvWaves == kKvBQ * T::WR && TBLK * 1024 * kKvWaves == D * T::WT, "fill blocks");
-  // three tiles: t (softmax, dV/dK operands), t+1 (S/dP operands), t+2 (filling)
-  __shared__ __attribute__((aligned(1024))) char lds[3 * T::BYTES];
+  // four tiles: t (softmax, dV/dK operands), t+1 (S/dP operands), t+2 and t+3
+  // (filling: a fill has two iterations to land)
+  __shared__ __attribute__((aligned(1024))) char lds[kKvBufs * T::BYTES];
+  constexpr int kFillOps = 2 * QBLK + 2 * TBLK + 1;   // loads per wavefront per fill
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   const int qlast = j0 + (nt - 1) * kKvBQ;       // first query of the last tile
   fill(0, j0);
   fill(1, min(j0 + kKvBQ, qlast));
-  tiles::dma_wait();
-  __syncthreads();
+  fill(2, min(j0 + 2 * kKvBQ, qlast));
+  tiles::wait_fills_barrier<kFillOps>();   // tiles 0 and 1 landed
   // S = Q~ K~^T, dP = dO~ V~^T of the first tile (lane = one key, 16 query rows)
   f32x16 sv = (f32x16){}, dp = (f32x16){};
 #pragma unroll
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
 
   // Iteration t.  One wavefront per SIMD has no other wavefront to hide its
   // latencies behind, so the body is one basic block in a fixed issue order:
-  //  1. fill of tile t+2 (into the buffer tile t-1 used);
+  //  1. fill of tile t+3 (into the buffer tile t-1 used);
   //  2. LDS reads of tile t's row pairs;
   //  3. the NC dV/dK products of tile t-1 (operands already in registers),
   //     each followed by one LDS read of tile t+1's S/dP operands -- the
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   //     of EPS of this lane's values of tile t (VALU work that runs while the
   //     products occupy the matrix core) and two LDS reads of tile t's dV/dK
   //     operands;
-  //  5. wait for the fill, barrier.
+  //  5. wait for the fill of tile t+2 (issued one iteration earlier), barrier.
   // Every wavefront updates its accumulators on every tile; the causal mask is
   // applied on the first kKvBK/kKvBQ tiles only (on later tiles every query
   // follows every key of the block); the fill past the last tile repeats the
@@ -328,8 +331,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   auto iteration = [&](int t, auto mask) {
     constexpr bool MASK = decltype(mask)::value;
     const int q0 = j0 + t * kKvBQ;
-    const int jc = t % 3, jn = jc == 2 ? 0 : jc + 1, jf = jn == 2 ? 0 : jn + 1;
-    fill(jf, min(q0 + 2 * kKvBQ, qlast));
+    const int jc = t & (kKvBufs - 1), jn = (t + 1) & (kKvBufs - 1), jf = (t + 3) & (kKvBufs - 1);
+    fill(jf, min(q0 + 3 * kKvBQ, qlast));
     const char *cur = lds + jc * T::BYTES;
     const char *nxt = lds + jn * T::BYTES;
     float4 r4[8];   // (LSE log2 e, delta) of rows 8 g4 + 4 hf + {0,1} and {2,3}
@@ -371,14 +374,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
     }
     sv = sv_n;
     dp = dp_n;
-    tiles::dma_wait();
-    __syncthreads();
+    tiles::wait_fills_barrier<kFillOps>();   // tile t+2 landed; tile t+3 may be in flight
   };
   const int nm = min(nt, kKvBK / kKvBQ);
   for (int t = 0; t < nm; ++t) iteration(t, Flag<true>{});
   for (int t = nm; t < nt; ++t) iteration(t, Flag<false>{});
 #pragma unroll
   for (int k = 0; k < NC; ++k) dvdk(k);
+  tiles::dma_wait();   // the fills past the last tile, before the work-group exits
 
   if (kj >= S) return;
   const float scale = 1.f / sqrtf((float)D);
