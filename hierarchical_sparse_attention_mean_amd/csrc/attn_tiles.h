@@ -6,21 +6,27 @@
 // contiguous 1 KB block and no registers hold the data in flight.  Since the
 // blocks are contiguous, LDS rows cannot be padded; bank conflicts are avoided
 // instead by XOR-swizzling the 16-byte chunks of each row: logical chunk c of
-// row r is stored at chunk c ^ swz(r).  The LDS has 64 four-byte banks and
-// serves a 16-byte read for 16 lanes per cycle, and the MFMA operand reads have
-// 16 consecutive lanes on 16 consecutive rows at the same logical chunk, so
-// swz is chosen to put those 16 reads in 16 different 16-byte bank groups: for
-// W-byte rows, row r starts at bank group (r * W / 16) mod 16 and swz adds the
-// remaining spread, swz(r) = (r / (256 / W)) mod (W / 16).
+// row r is stored at chunk c ^ swz(r).  The LDS has 64 four-byte banks (16
+// groups of 16 bytes).  Two read patterns must be conflict-free:
+//  - MFMA operand reads (ds_read_b128, 16 lanes per cycle): 16 consecutive
+//    rows at the same logical chunk, so swz must take 16 different values
+//    over any 16 consecutive rows (per bank-alignment class of the rows);
+//  - transposing reads (ds_read_b64_tr_b16, 32 lanes per cycle): 4 consecutive
+//    rows x 4 consecutive chunks (64 bytes), so the 4 rows must land in 4
+//    different 4-chunk groups.
+// For 256-byte rows swz(r) = ((r & 3) << 2) | ((r >> 2) & 3); for 128-byte rows
+// (two rows per 16 bank groups) the same idea on x = (r >> 1) & 7.
 //
 // MFMA operand reads (v_mfma_f32_32x32x16_bf16): lane (ln, hf) = (lane % 32,
 // lane / 32) reads row ln of a 32-row block, logical chunk 2c + hf, i.e. the 8
 // consecutive contraction elements 16c + 8hf .. +7 -- for row-major tiles
-// (contraction over d) directly.  Transposed tiles (contraction over keys or
-// queries) are stored by their producers with bits 2 and 3 of the column index
-// swapped (see perm16), which turns the MFMA's split k-chunk
-// {16c + 4hf + 0..3, 16c + 8 + 4hf + 0..3} -- forced by the 32x32 result
-// layout of the probabilities -- into the same single 16-byte read.
+// (contraction over d) directly.  Operands contracted over keys or queries,
+// whose B operand is a probability block in registers, need the contraction
+// elements in the order {16c + 4hf + 0..3, 16c + 8 + 4hf + 0..3} (forced by the
+// 32x32 result layout): transposed copies in global memory are stored by their
+// producers with bits 2 and 3 of the column index swapped (see perm16), which
+// makes that one 16-byte read; a row-major tile gives the same operand with
+// two transposing reads (tr_frag).
 #pragma once
 
 #include "lh_internal.h"
@@ -36,9 +42,14 @@ __host__ __device__ __forceinline__ int perm16(int m) { return (m & ~12) | ((m &
 
 // chunk swizzle for rows of W bytes (W = 64, 128 or 256)
 template <int W>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ __forceinline__ int swz(int r) {
   static_assert(W == 64 || W == 128 || W == 256, "row width");
-  return (r / (256 / W)) & (W / 16 - 1);
+  if constexpr (W == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if constexpr (W == 128) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  }
+  return (r >> 2) & 3;
 }
 
 // byte offset of (row r, logical 16-byte chunk c) in a tile of W-byte rows
@@ -49,6 +60,39 @@ __device__ __forceinline__ int tile_off(int r, int c) {
 
 __device__ __forceinline__ bf16x8 lds_frag(const char *tile, int off) {
   return *reinterpret_cast<const bf16x8 *>(tile + off);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// 4k + i / 4, k = 0..3.  So if lanes 4k .. 4k+3 of a group address the 16
+// consecutive elements [c0, c0 + 16) of row r0 + k, lane i receives column
+// c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 lds_tr4(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+}
+
+// Per-lane byte offset, in a row-major tile of W-byte bf16 rows, of the
+// transposing read that gives lane (ln, hf) column c0 + ln of rows
+// r0 + 4 hf + 0..3 (lanes 4k + m of each 16-lane group address row r0 + 4 hf + k,
+// columns c0 + 16 (group & 1) + 4m .. +3).
+template <int W>
+__device__ __forceinline__ int tr_off(int r0, int c0) {
+  const int l = threadIdx.x & 63, li = l & 15;
+  const int r = r0 + 4 * (l >> 5) + (li >> 2);
+  const int col = c0 + 16 * ((l >> 4) & 1) + 4 * (li & 3);
+  return r * W + 16 * ((col >> 3) ^ swz<W>(r)) + 2 * (col & 7);
+}
+
+// MFMA A operand of X^T for a row-major tile X (rows = contraction index):
+// lane (ln, hf) gets column c0 + ln of rows {r0 + 4hf + 0..3, r0 + 8 + 4hf + 0..3}
+// -- the probability-register order above -- from two transposing reads at the
+// per-lane offsets lo = tr_off(r0, c0), hi = tr_off(r0 + 8, c0).
+__device__ __forceinline__ bf16x8 tr_frag(const char *tile, int lo, int hi) {
+  const s16x8 v = __builtin_shufflevector(lds_tr4(tile + lo), lds_tr4(tile + hi), 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // 32-bit LDS address of a pointer into __shared__ memory, the same in every lane

@@ -40,6 +40,11 @@ using tiles::f32x16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
@@ -165,29 +170,41 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
+// Work-group: 128 keys, 4 pairs of wavefronts, one pair per 32 keys and per
+// SIMD.  In a pair, the "P" wavefront holds the keys' K~ rows and the dV~
+// accumulators, the "dS" wavefront their V~ rows and the dK~ accumulators (each
+// needs half the registers of doing both, so two wavefronts fit on a SIMD and
+// the hardware interleaves them).  Per 32-query tile t:
+//   P  wavefront:  S = Q~ K~^T, P = exp2(S log2(e)/sqrt(d) - LSE log2(e))
+//                  (causally masked), P -> LDS exchange (fp32),
+//                  dV~^T += dO~^T P;
+//   dS wavefront:  dP = dO~ V~^T for tile t, and for tile t-1 (one barrier
+//                  behind, so P(t-1) is in the exchange):
+//                  dS = P o (dP - delta), dK~^T += Q~^T dS.
+// Each wavefront issues 16 of the tile's 32 MFMAs.  Only the row-major Q~ and
+// dO~ tiles are streamed: the transposed operands dO~^T and Q~^T come from the
+// same LDS tiles through transposing reads (attn_tiles.h), which halves the
+// bytes per tile -- the kernel is otherwise bound by streaming the query tiles
+// (1 KB per query per 128 keys).  Tiles go through a ring of four LDS buffers
+// (t-1: dS side, t: both, t+1: landed, t+2: filling), the exchange is
+// double-buffered by tile parity.
+constexpr int kKvPairs = 4;
+constexpr int kKvWaves = 2 * kKvPairs;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvBK = 32 * kKvWaves;
-constexpr int kKvBQ = 32;   // query rows per tile
-constexpr int kKvBufs = 4;  // tiles in LDS
+constexpr int kKvBK = 32 * kKvPairs;   // keys per work-group
+constexpr int kKvBQ = 32;              // query rows per tile
+constexpr int kKvBufs = 4;             // tiles in LDS
+constexpr int kXBytes = 16 * 4 * 64;   // one pair's P: 16 fp32 per lane
 
-// One query tile in LDS: Q~ and dO~ rows, their transposes, and the rows'
-// (LSE log2(e), delta) pairs.
+// One query tile in LDS: Q~ and dO~ rows, LSE log2(e) and delta of the rows.
 template <int D>
 struct DkvTile {
-  static constexpr int WR = 2 * D;       // bytes per Q~ / dO~ row
-  static constexpr int WT = 2 * kKvBQ;   // bytes per Q~^T / dO~^T row
+  static constexpr int WR = 2 * D;   // bytes per Q~ / dO~ row
   static constexpr int Q = 0;
   static constexpr int G = Q + kKvBQ * WR;
-  static constexpr int QT = G + kKvBQ * WR;
-  static constexpr int GT = QT + D * WT;
-  static constexpr int RS = GT + D * WT;
-  static constexpr int BYTES = RS + 8 * kKvBQ;
-};
-
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
+  static constexpr int LS = G + kKvBQ * WR;
+  static constexpr int DL = LS + 4 * kKvBQ;
+  static constexpr int BYTES = DL + 4 * kKvBQ;
 };
 
 template <int D>
@@ -195,207 +212,193 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
                                                                  const uint16_t *__restrict__ qt,
                                                                  const uint16_t *__restrict__ kt,
                                                                  const uint16_t *__restrict__ vt,
-                                                                 const uint16_t *__restrict__ qtt,
                                                                  const uint16_t *__restrict__ dotb,
-                                                                 const uint16_t *__restrict__ dott,
                                                                  const float *__restrict__ rows,
                                                                  float *__restrict__ dkt, float *__restrict__ dvt) {
   using T = DkvTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  constexpr int NC = 4 * DB;   // dV/dK products per tile
-  static_assert(NC == 2 * KC, "one S/dP operand read per dV/dK product");
-  constexpr int EPS = 16 / KC;                                // softmax values per S/dP step
-  constexpr int QBLK = kKvBQ * T::WR / 1024 / kKvWaves;       // 1 KB fill blocks per wavefront: Q~, dO~
-  constexpr int TBLK = D * T::WT / 1024 / kKvWaves;           // ... Q~^T, dO~^T
-  static_assert(QBLK * 1024 * kKvWaves == kKvBQ * T::WR && TBLK * 1024 * kKvWaves == D * T::WT, "fill blocks");
-  // four tiles: t (softmax, dV/dK operands), t+1 (S/dP operands), t+2 and t+3
-  // (filling: a fill has two iterations to land)
-  __shared__ __attribute__((aligned(1024))) char lds[kKvBufs * T::BYTES];
-  constexpr int kFillOps = 2 * QBLK + 2 * TBLK + 1;   // loads per wavefront per fill
+  static_assert(4 * DB == 2 * KC, "as many dV/dK products as S/dP products");
+  constexpr int QB = kKvBQ * T::WR / 1024;   // 1 KB fill blocks of a Q~ or dO~ tile
+  static_assert(QB * 1024 == kKvBQ * T::WR && kKvWaves % QB == 0 || QB % kKvWaves == 0, "fill blocks");
+  constexpr int QBLK = (QB + kKvWaves - 1) / kKvWaves;   // blocks per wavefront (duplicated if QB < 8)
+  constexpr int kFillOps = 2 * QBLK + 1;                  // loads per wavefront per fill
+  __shared__ __attribute__((aligned(1024))) char lds[kKvBufs * T::BYTES + 2 * kKvPairs * kXBytes];
+  char *xch = lds + kKvBufs * T::BYTES;
   const int h = blockIdx.x % BH;
   const int kb = blockIdx.x / BH;   // first key blocks see the most queries: launched first
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int j0 = kb * kKvBK, kw = j0 + 32 * w, kj = kw + ln;
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wu % kKvPairs;   // wavefronts w and w + 4 share a SIMD
+  const bool dsw = wu >= kKvPairs;  // the dS wavefront of the pair
+  const int j0 = kb * kKvBK, kw = j0 + 32 * pair, kj = kw + ln;
   const long long hbS = (long long)h * S;    // dK~, dV~: S rows per head
   const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~, row pairs: Sv rows per head (rows S..Sv-1 zero)
   const char *qh = reinterpret_cast<const char *>(qt + hbV * D);
   const char *gh = reinterpret_cast<const char *>(dotb + hbV * D);
-  const char *qth = reinterpret_cast<const char *>(qtt + (long long)h * D * Sv);
-  const char *gth = reinterpret_cast<const char *>(dott + (long long)h * D * Sv);
   const char *rh = reinterpret_cast<const char *>(rows + 2 * hbV);
   const unsigned lbase = tiles::lds_addr(lds);
 
-  // Fills: per-lane source offsets are loop invariant; the tile's base address
-  // and the LDS destination are scalars.  Query tiles start below S and are 32
-  // rows, so they never pass the padded Sv rows; a padding query (zero Q~, dO~,
-  // LSE and delta) adds exactly 0.  Every wavefront issues the same 256-byte
-  // fill of the row pairs (identical bytes), so the fill has no branch.
-  unsigned vq[QBLK], vtr[TBLK];
+  // Fills (every wavefront issues the same number of loads; with fewer blocks
+  // than wavefronts some blocks are loaded twice, identical bytes).  Query
+  // tiles start below S and are 32 rows, so they never pass the padded Sv
+  // rows; a padding query (zero Q~, dO~, LSE and delta) adds exactly 0.  The
+  // row pairs (LSE log2 e, delta) are split on the way in: lane l < 32 loads
+  // the LSE of row l, lane 32 + l its delta, so LS and DL are adjacent arrays.
+  unsigned vq[QBLK];
+  int bq[QBLK];
 #pragma unroll
-  for (int i = 0; i < QBLK; ++i) vq[i] = tiles::dma_voff<T::WR>(wu + i * kKvWaves, T::WR);
-#pragma unroll
-  for (int i = 0; i < TBLK; ++i) vtr[i] = tiles::dma_voff<T::WT>(wu + i * kKvWaves, 2u * Sv);
-  const unsigned vrs = 4u * lane;
+  for (int i = 0; i < QBLK; ++i) {
+    bq[i] = (wu + i * kKvWaves) % QB;
+    vq[i] = tiles::dma_voff<T::WR>(bq[i], T::WR);
+  }
+  const unsigned vrs = 8u * ln + 4u * hf;
   auto fill = [&](int jb, int q0) {
     const unsigned m = lbase + jb * T::BYTES;
 #pragma unroll
     for (int i = 0; i < QBLK; ++i) {
-      const unsigned blk = 1024u * (wu + i * kKvWaves);
-      tiles::lds_load_s<16>(qh + (long long)q0 * T::WR, vq[i], m + T::Q + blk);
-      tiles::lds_load_s<16>(gh + (long long)q0 * T::WR, vq[i], m + T::G + blk);
+      tiles::lds_load_s<16>(qh + (long long)q0 * T::WR, vq[i], m + T::Q + 1024u * bq[i]);
+      tiles::lds_load_s<16>(gh + (long long)q0 * T::WR, vq[i], m + T::G + 1024u * bq[i]);
     }
-#pragma unroll
-    for (int i = 0; i < TBLK; ++i) {
-      const unsigned blk = 1024u * (wu + i * kKvWaves);
-      tiles::lds_load_s<16>(qth + 2LL * q0, vtr[i], m + T::QT + blk);
-      tiles::lds_load_s<16>(gth + 2LL * q0, vtr[i], m + T::GT + blk);
-    }
-    tiles::lds_load_s<4>(rh + 8LL * q0, vrs, m + T::RS);
+    tiles::lds_load_s<4>(rh + 8LL * q0, vrs, m + T::LS);
   };
 
-  // per-lane LDS read offsets (loop invariant): S/dP operands (row ln, chunk
-  // 2c+hf of a row-major tile) and dV/dK operands (row 32b+ln, chunk 2cc+hf of
-  // a transposed tile, c = cc DB + b)
-  int oq[KC], ot[KC];
+  // per-lane LDS read offsets: row-major operands (row ln, chunk 2c+hf) and
+  // the transposing reads of query chunk 0 (chunk cc adds 16 cc rows), d block b
+  int oq[KC], otr[DB][2];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    oq[c] = tiles::tile_off<T::WR>(ln, 2 * c + hf);
-    ot[c] = tiles::tile_off<T::WT>(32 * (c % DB) + ln, 2 * (c / DB) + hf);
-  }
-  const int ors = T::RS + 32 * hf;   // row pairs 8 g4 + 4 hf + 0..3 at ors + 64 g4
-
-  // K~, V~ rows of this lane's key: B operands of S and dP (keys past Sv read as zero)
-  bf16x8 kf[KC], vf[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (kj < Sv) {
-      kf[c] = *reinterpret_cast<const bf16x8 *>(kt + (hbV + kj) * D + 16 * c + 8 * hf);
-      vf[c] = *reinterpret_cast<const bf16x8 *>(vt + (hbV + kj) * D + 16 * c + 8 * hf);
-    } else {
-      kf[c] = (bf16x8){};
-      vf[c] = (bf16x8){};
-    }
-  }
-  const float c2 = kLog2e / sqrtf((float)D);
-  f32x16 adk[DB], adv[DB];
+  for (int c = 0; c < KC; ++c) oq[c] = tiles::tile_off<T::WR>(ln, 2 * c + hf);
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    adk[b] = (f32x16){};
-    adv[b] = (f32x16){};
+    otr[b][0] = tiles::tr_off<T::WR>(0, 32 * b);
+    otr[b][1] = tiles::tr_off<T::WR>(8, 32 * b);
   }
-  // dV/dK operands of the previous tile: P and dS (B operands, from the
-  // softmax) and the dO~^T, Q~^T chunks (A operands, from LDS)
-  bf16x8 pf[2], dsf[2], fgt[KC], fqt[KC];
+  // this lane's part of its pair's exchange slot: 16 fp32 as 4 x 16 bytes,
+  // [k][lane] so that consecutive lanes hit consecutive bank groups
+  const int ox = pair * kXBytes + 16 * lane;
+
+  // this lane's key row of K~ (P wavefront) or V~ (dS wavefront): B operand
+  // of S = Q~ K~^T or dP = dO~ V~^T (keys past Sv read as zero)
+  bf16x8 kv[KC];
+  {
+    const uint16_t *src = (dsw ? vt : kt) + (hbV + kj) * D + 8 * hf;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) pf[c] = dsf[c] = (bf16x8){};
+    for (int c = 0; c < KC; ++c) kv[c] = (kj < Sv) ? *reinterpret_cast<const bf16x8 *>(src + 16 * c) : (bf16x8){};
+  }
+  tiles::dma_wait();
+  const float c2 = kLog2e / sqrtf((float)D);
+  f32x16 acc[DB];   // dV~^T (P wavefront) or dK~^T (dS wavefront) of the pair's 32 keys
 #pragma unroll
-  for (int c = 0; c < KC; ++c) fgt[c] = fqt[c] = (bf16x8){};
-  // k-th dV/dK product of the previous tile
-  auto dvdk = [&](int k) {
-    const int c = k >> 1, cc = c / DB, b = c % DB;
-    if (k & 1) adk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fqt[c], dsf[cc], adk[b], 0, 0, 0);
-    else adv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fgt[c], pf[cc], adv[b], 0, 0, 0);
-  };
+  for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
 
   const int nt = (S - j0 + kKvBQ - 1) / kKvBQ;   // query tiles from the block's first key to S
   const int qlast = j0 + (nt - 1) * kKvBQ;       // first query of the last tile
   fill(0, j0);
   fill(1, min(j0 + kKvBQ, qlast));
-  fill(2, min(j0 + 2 * kKvBQ, qlast));
-  tiles::wait_fills_barrier<kFillOps>();   // tiles 0 and 1 landed
-  // S = Q~ K~^T, dP = dO~ V~^T of the first tile (lane = one key, 16 query rows)
-  f32x16 sv = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(lds + T::Q, oq[c]), kf[c], sv, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(lds + T::G, oq[c]), vf[c], dp, 0, 0, 0);
-  }
+  tiles::wait_fills_barrier<kFillOps>();   // tile 0 landed
 
-  // Iteration t.  One wavefront per SIMD has no other wavefront to hide its
-  // latencies behind, so the body is one basic block in a fixed issue order:
-  //  1. fill of tile t+3 (into the buffer tile t-1 used);
-  //  2. LDS reads of tile t's row pairs;
-  //  3. the NC dV/dK products of tile t-1 (operands already in registers),
-  //     each followed by one LDS read of tile t+1's S/dP operands -- the
-  //     products cover the read latency;
-  //  4. KC steps, each issuing one S/dP product pair of tile t+1, the softmax
-  //     of EPS of this lane's values of tile t (VALU work that runs while the
-  //     products occupy the matrix core) and two LDS reads of tile t's dV/dK
-  //     operands;
-  //  5. wait for the fill of tile t+2 (issued one iteration earlier), barrier.
-  // Every wavefront updates its accumulators on every tile; the causal mask is
-  // applied on the first kKvBK/kKvBQ tiles only (on later tiles every query
-  // follows every key of the block); the fill past the last tile repeats the
-  // last tile and the S/dP products past it are dropped.
-  auto iteration = [&](int t, auto mask) {
-    constexpr bool MASK = decltype(mask)::value;
-    const int q0 = j0 + t * kKvBQ;
-    const int jc = t & (kKvBufs - 1), jn = (t + 1) & (kKvBufs - 1), jf = (t + 3) & (kKvBufs - 1);
-    fill(jf, min(q0 + 3 * kKvBQ, qlast));
-    const char *cur = lds + jc * T::BYTES;
-    const char *nxt = lds + jn * T::BYTES;
-    float4 r4[8];   // (LSE log2 e, delta) of rows 8 g4 + 4 hf + {0,1} and {2,3}
+  // 32x32 product over d: rows of a row-major tile (A operand) times this
+  // lane's key row (B operand)
+  auto rowprod = [&](const char *tile) {
+    bf16x8 f[KC];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      r4[2 * g4] = *reinterpret_cast<const float4 *>(cur + ors + 64 * g4);
-      r4[2 * g4 + 1] = *reinterpret_cast<const float4 *>(cur + ors + 64 * g4 + 16);
-    }
-    bf16x8 fq[KC], fg[KC];
+    for (int c = 0; c < KC; ++c) f[c] = tiles::lds_frag(tile, oq[c]);
+    f32x16 r = (f32x16){};
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      dvdk(k);
-      if (k & 1) fg[k >> 1] = tiles::lds_frag(nxt + T::G, oq[k >> 1]);
-      else fq[k >> 1] = tiles::lds_frag(nxt + T::Q, oq[k >> 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    f32x16 sv_n = (f32x16){}, dp_n = (f32x16){};
+    for (int c = 0; c < KC; ++c) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], kv[c], r, 0, 0, 0);
+    return r;
+  };
+  // acc^T += X^T x for a row-major tile X (rows = the tile's queries) and the
+  // bf16 B operand chunks x[cc] (16 queries each, probability-register order)
+  auto colprod = [&](const char *tile, const bf16x8 *x) {
+    bf16x8 f[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      sv_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], kf[c], sv_n, 0, 0, 0);
-      dp_n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fg[c], vf[c], dp_n, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < EPS; ++u) {
-        const int i = EPS * c + u;   // register of the 32x32 block: query row 8 g4 + 4 hf + e
-        const int g4 = i >> 2, e = i & 3;
-        const float4 &rp = r4[2 * g4 + (e >> 1)];
-        const float ls = (e & 1) ? rp.z : rp.x;
-        const float dl = (e & 1) ? rp.w : rp.y;
-        float pj = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ls));
-        if constexpr (MASK) {
-          if (q0 + 8 * g4 + 4 * hf + e < kj) pj = 0.f;
-        }
-        pf[i >> 3][i & 7] = (__bf16)pj;
-        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dl));
-      }
-      fgt[c] = tiles::lds_frag(cur + T::GT, ot[c]);
-      fqt[c] = tiles::lds_frag(cur + T::QT, ot[c]);
-      __builtin_amdgcn_sched_barrier(0);
+      const int cc = c / DB, b = c % DB;
+      f[c] = tiles::tr_frag(tile + 16 * cc * T::WR, otr[b][0], otr[b][1]);
     }
-    sv = sv_n;
-    dp = dp_n;
-    tiles::wait_fills_barrier<kFillOps>();   // tile t+2 landed; tile t+3 may be in flight
-  };
-  const int nm = min(nt, kKvBK / kKvBQ);
-  for (int t = 0; t < nm; ++t) iteration(t, Flag<true>{});
-  for (int t = nm; t < nt; ++t) iteration(t, Flag<false>{});
 #pragma unroll
-  for (int k = 0; k < NC; ++k) dvdk(k);
+    for (int c = 0; c < KC; ++c)
+      acc[c % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], x[c / DB], acc[c % DB], 0, 0, 0);
+  };
+
+  if (!dsw) {
+    // ---- P wavefront: S, P, exchange, dV ----
+    auto iter_p = [&](int t, auto mask) {
+      constexpr bool MASK = decltype(mask)::value;
+      const int q0 = j0 + t * kKvBQ;
+      const char *cur = lds + (t % kKvBufs) * T::BYTES;
+      fill((t + 2) % kKvBufs, min(q0 + 2 * kKvBQ, qlast));   // past the end: a repeat of the last tile
+      float4 l4[4];   // LSE log2 e of rows 8 g4 + 4 hf + 0..3
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) l4[g4] = *reinterpret_cast<const float4 *>(cur + T::LS + 4 * (8 * g4 + 4 * hf));
+      const f32x16 sv = rowprod(cur + T::Q);
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int g4 = i >> 2, e = i & 3;
+        const float ls = e == 0 ? l4[g4].x : e == 1 ? l4[g4].y : e == 2 ? l4[g4].z : l4[g4].w;
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ls));
+        if constexpr (MASK) {
+          if (q0 + 8 * g4 + 4 * hf + e < kj) p[i] = 0.f;
+        }
+      }
+      char *x = xch + (t & 1) * (kKvPairs * kXBytes) + ox;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<float4 *>(x + 1024 * k) = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
+      bf16x8 pf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (__bf16)p[i];
+      colprod(cur + T::G, pf);   // dV~^T += dO~^T P
+      tiles::wait_fills_barrier<kFillOps>();   // tile t+1 landed
+    };
+    const int nm = min(nt, kKvBK / kKvBQ);   // tiles that reach below some key of the block: masked
+    for (int t = 0; t < nm; ++t) iter_p(t, Flag<true>{});
+    for (int t = nm; t < nt; ++t) iter_p(t, Flag<false>{});
+  } else {
+    // ---- dS wavefront: dP of tile t; dS and dK of tile t-1 ----
+    f32x16 dpp = (f32x16){};   // dP of the previous tile
+    auto ds_dk = [&](int t) {   // dS and dK~ of tile t (its P in the exchange)
+      const char *tb = lds + (t % kKvBufs) * T::BYTES;
+      const char *x = xch + (t & 1) * (kKvPairs * kXBytes) + ox;
+      float4 p4[4], d4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        p4[k] = *reinterpret_cast<const float4 *>(x + 1024 * k);
+        d4[k] = *reinterpret_cast<const float4 *>(tb + T::DL + 4 * (8 * k + 4 * hf));
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int g4 = i >> 2, e = i & 3;
+        const float pj = e == 0 ? p4[g4].x : e == 1 ? p4[g4].y : e == 2 ? p4[g4].z : p4[g4].w;
+        const float dl = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
+        dsf[i >> 3][i & 7] = (__bf16)(pj * (dpp[i] - dl));
+      }
+      colprod(tb + T::Q, dsf);   // dK~^T += Q~^T dS
+    };
+    for (int t = 0; t < nt; ++t) {
+      const int q0 = j0 + t * kKvBQ;
+      const char *cur = lds + (t % kKvBufs) * T::BYTES;
+      fill((t + 2) % kKvBufs, min(q0 + 2 * kKvBQ, qlast));
+      if (t > 0) ds_dk(t - 1);
+      dpp = rowprod(cur + T::G);   // dP = dO~ V~^T
+      tiles::wait_fills_barrier<kFillOps>();
+    }
+    ds_dk(nt - 1);
+  }
   tiles::dma_wait();   // the fills past the last tile, before the work-group exits
 
   if (kj >= S) return;
-  const float scale = 1.f / sqrtf((float)D);
-  float *krow = dkt + (hbS + kj) * D;
-  float *vrow = dvt + (hbS + kj) * D;
+  const float scale = dsw ? 1.f / sqrtf((float)D) : 1.f;
+  float *orow = (dsw ? dkt : dvt) + (hbS + kj) * D;
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = 32 * b + 8 * g + 4 * hf;
-      *reinterpret_cast<float4 *>(krow + dd) = make_float4(adk[b][4 * g] * scale, adk[b][4 * g + 1] * scale,
-                                                           adk[b][4 * g + 2] * scale, adk[b][4 * g + 3] * scale);
-      *reinterpret_cast<float4 *>(vrow + dd) =
-          make_float4(adv[b][4 * g], adv[b][4 * g + 1], adv[b][4 * g + 2], adv[b][4 * g + 3]);
+      *reinterpret_cast<float4 *>(orow + dd) = make_float4(acc[b][4 * g] * scale, acc[b][4 * g + 1] * scale,
+                                                           acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
     }
 }
 
@@ -412,8 +415,8 @@ hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, co
     if (d == 128) k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
     else k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
   } else {           // dK~, dV~
-    if (d == 128) k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
-    else k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, qT, g, gT, rows, dkt, dvt);
+    if (d == 128) k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);
+    else k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);
   }
   return hipGetLastError();
 }
