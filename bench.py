@@ -226,16 +226,11 @@ def main() -> int:
              "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
     stream = torch.cuda.current_stream()
     if args.dense:
-        if io == torch.bfloat16:   # V^T, columns in the kernel's order (bits 2 and 3 of the index swapped)
-            col = torch.arange(N, device=dev)
-            perm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1)
-            vt_dense = v.reshape(BH, N, d).transpose(1, 2)[:, :, perm].contiguous()
-        else:
-            vt_dense = v.reshape(BH, N, d)
         od = torch.empty((BH, N, d), dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        st = lh.lh_attention_forward(q.reshape(BH, N, d), kk.reshape(BH, N, d), vt_dense, od, None, BH, N, d, io)
+        st = lh.lh_attention_forward(q.reshape(BH, N, d), kk.reshape(BH, N, d), v.reshape(BH, N, d), od, None, BH, N,
+                                     d, io)
         e1.record(stream)
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1)
@@ -243,7 +238,7 @@ def main() -> int:
         extra["dense_attn_fwd_tflops"] = attention_flops(N, d, BH) / (dms * 1e-3) / 1e12
         extra["lighthouse_fwd_speedup_vs_dense"] = dms / ms_fwd
         log(f"[bench] dense causal attention at S=N: {dms:.1f} ms")
-        del od, vt_dense
+        del od
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -12,10 +12,10 @@
 // in-lane plus one exchange between the two half-waves.  The probabilities P^T
 // (converted to bf16) are then the B operand, straight from registers, of
 // O^T += V~^T P^T, whose result again gives each lane one query column -- the
-// running max, sum and rescale factor are per-lane scalars.  V~^T comes
-// pre-transposed from the gather ([d][Sv], Sv a multiple of 64, zero padded,
-// columns in the perm16 order of attn_tiles.h) so both LDS operands are single
-// 16-byte reads per lane.
+// running max, sum and rescale factor are per-lane scalars.  Both K~ and V~
+// are staged as row-major tiles; the V~^T operand comes from the V~ tile by
+// transposing LDS reads in the key order of the probability registers
+// (attn_tiles.h).
 //
 // Work-group: 8 wavefronts x 32 queries = 256 query rows (one work-group per
 // CU); key/value tiles of 64 rows in a ring of four LDS buffers filled by
@@ -55,14 +55,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kFwdBufs = 4;   // key/value tiles in LDS
 constexpr int kWin = 8;       // LDS operand fragments in flight per wavefront
 
-// One key/value tile in LDS: K~ rows, then V~^T rows (keys along the row).
+// One key/value tile in LDS: K~ rows, then V~ rows.
 template <int D>
 struct FwdTile {
-  static constexpr int WK = 2 * D;    // bytes per K~ row
-  static constexpr int WV = 2 * BN;   // bytes per V~^T row
+  static constexpr int WK = 2 * D;   // bytes per K~ / V~ row
   static constexpr int K = 0;
   static constexpr int V = BN * WK;
-  static constexpr int BYTES = V + D * WV;
+  static constexpr int BYTES = 2 * BN * WK;
 };
 
 template <bool B>
@@ -71,21 +70,20 @@ struct Flag {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sq, int Sv, int BH,
+__global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sq, int BH,
                                                                const uint16_t *__restrict__ qt,
                                                                const uint16_t *__restrict__ kt,
-                                                               const uint16_t *__restrict__ vtt,
+                                                               const uint16_t *__restrict__ vt,
                                                                float *__restrict__ ot, float *__restrict__ lse) {
   using T = FwdTile<D>;
   constexpr int KC = D / 16;          // 16-wide d chunks of the Q.K contraction
   constexpr int DB = D / 32;          // 32-row d blocks of O^T
   constexpr int NS = 2 * KC;          // S^T products (= K~ fragments) per tile
-  constexpr int NF = NS + 4 * DB;     // LDS fragments per tile: K~, then V~^T
+  constexpr int NF = NS + 4 * DB;     // LDS operand fragments per tile: K~, then V~^T
   static_assert(NS + kWin <= NF, "the window reaches the next tile only in the O^T phase");
-  constexpr int KBLK = BN * T::WK / 1024 / kWaves;   // 1 KB fill blocks per wavefront: K~
-  constexpr int VBLK = D * T::WV / 1024 / kWaves;    // ... V~^T
-  static_assert(KBLK * 1024 * kWaves == BN * T::WK && VBLK * 1024 * kWaves == D * T::WV, "fill blocks");
-  constexpr int kFillOps = KBLK + VBLK;              // loads per wavefront per fill
+  constexpr int KBLK = BN * T::WK / 1024 / kWaves;   // 1 KB fill blocks per wavefront, K~ and V~ each
+  static_assert(KBLK * 1024 * kWaves == BN * T::WK, "fill blocks");
+  constexpr int kFillOps = 2 * KBLK;                 // loads per wavefront per fill
   __shared__ __attribute__((aligned(1024))) char lds[kFwdBufs * T::BYTES];
 
   const int nqb = (S + BM - 1) / BM;
@@ -98,47 +96,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sq, in
   const int qw = q0 + 32 * w;   // first query of this wavefront
   const int qi = qw + ln;       // this lane's query
   const long long hbS = (long long)h * S;   // O~, LSE: S rows per head
-  const uint16_t *qh = qt + (long long)h * Sq * D;   // Q~, K~: Sq rows per head
+  const uint16_t *qh = qt + (long long)h * Sq * D;   // Q~, K~, V~: Sq rows per head
   const char *kh = reinterpret_cast<const char *>(kt + (long long)h * Sq * D);
-  const char *vh = reinterpret_cast<const char *>(vtt + (long long)h * D * Sv);
+  const char *vh = reinterpret_cast<const char *>(vt + (long long)h * Sq * D);
   const unsigned lbase = tiles::lds_addr(lds);
 
-  // Fills.  K~ rows past S are clamped to row S-1 (finite; those keys are
-  // causally masked), V~^T columns past S are the zero padding up to Sv.
+  // Fills.  K~ and V~ rows past S are clamped to row S-1 (finite; those keys
+  // are causally masked: probability exactly 0).
   int kr[KBLK];
-  unsigned kc[KBLK], vo[VBLK];
+  unsigned kc[KBLK];
 #pragma unroll
   for (int i = 0; i < KBLK; ++i) {
     const int byte = (wu + i * kWaves) * 1024 + 16 * lane;
     kr[i] = byte / T::WK;
     kc[i] = 16u * (((byte % T::WK) / 16) ^ tiles::swz<T::WK>(kr[i]));
   }
-#pragma unroll
-  for (int i = 0; i < VBLK; ++i) vo[i] = tiles::dma_voff<T::WV>(wu + i * kWaves, 2u * Sv);
   auto fill = [&](int jb, int k0) {
     const unsigned m = lbase + jb * T::BYTES;
     const int rclamp = S - 1 - k0;
 #pragma unroll
-    for (int i = 0; i < KBLK; ++i)
-      tiles::lds_load_s<16>(kh + (long long)k0 * T::WK, (unsigned)min(kr[i], rclamp) * T::WK + kc[i],
-                            m + T::K + 1024u * (wu + i * kWaves));
-#pragma unroll
-    for (int i = 0; i < VBLK; ++i)
-      tiles::lds_load_s<16>(vh + 2LL * k0, vo[i], m + T::V + 1024u * (wu + i * kWaves));
+    for (int i = 0; i < KBLK; ++i) {
+      const unsigned vo = (unsigned)min(kr[i], rclamp) * T::WK + kc[i];
+      tiles::lds_load_s<16>(kh + (long long)k0 * T::WK, vo, m + T::K + 1024u * (wu + i * kWaves));
+      tiles::lds_load_s<16>(vh + (long long)k0 * T::WK, vo, m + T::V + 1024u * (wu + i * kWaves));
+    }
   };
 
-  // LDS fragment j of a tile: K~ rows 32 kb + ln, chunk 2c + hf (j = kb KC + c),
-  // then V~^T rows 32 b + ln, chunk 2c + hf (j = NS + c DB + b).  The swizzle of
-  // row 32 x + ln equals that of row ln, so the per-lane part depends on c only.
-  int ok[KC], ov[4];
+  // LDS operand fragment j of a tile: K~ rows 32 kb + ln, chunk 2c + hf
+  // (j = kb KC + c; the swizzle of row 32 x + ln equals that of row ln, so the
+  // per-lane offset depends on c only), then V~^T d rows 32 b + ln over the 16
+  // keys of chunk c (j = NS + c DB + b): two transposing reads of the V~ tile.
+  int ok[KC], ov[DB][2];
 #pragma unroll
   for (int c = 0; c < KC; ++c) ok[c] = tiles::tile_off<T::WK>(ln, 2 * c + hf);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) ov[c] = tiles::tile_off<T::WV>(ln, 2 * c + hf);
+  for (int b = 0; b < DB; ++b) {
+    ov[b][0] = tiles::tr_off<T::WK>(0, 32 * b);
+    ov[b][1] = tiles::tr_off<T::WK>(8, 32 * b);
+  }
   auto frag = [&](const char *buf, int j) -> bf16x8 {
     if (j < NS) return tiles::lds_frag(buf + T::K + 32 * (j / KC) * T::WK, ok[j % KC]);
-    const int jj = j - NS;
-    return tiles::lds_frag(buf + T::V + 32 * (jj % DB) * T::WV, ov[jj / DB]);
+    const int jj = j - NS, c = jj / DB, b = jj % DB;
+    return tiles::tr_frag(buf + T::V + 16 * c * T::WK, ov[b][0], ov[b][1]);
   };
 
   // Q~ fragment: B operand of S^T = K~ Q~^T (lane: query qi, d = 16c + 8hf .. +7)
@@ -249,16 +248,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd_mfma(int S, int Sq, in
 
 }  // namespace
 
-hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, int vstride, const void *qt, const void *kt, const void *vtt,
+hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st) {
   const int nqb = (S + BM - 1) / BM;
   dim3 grid(nqb * BH);
   if (d == 128)
-    k_attn_fwd_mfma<128><<<grid, kThreads, 0, st>>>(S, Sq, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
-                                                    (const uint16_t *)vtt, ot, lse);
+    k_attn_fwd_mfma<128><<<grid, kThreads, 0, st>>>(S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+                                                    (const uint16_t *)vt, ot, lse);
   else
-    k_attn_fwd_mfma<64><<<grid, kThreads, 0, st>>>(S, Sq, vstride, BH, (const uint16_t *)qt, (const uint16_t *)kt,
-                                                   (const uint16_t *)vtt, ot, lse);
+    k_attn_fwd_mfma<64><<<grid, kThreads, 0, st>>>(S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+                                                   (const uint16_t *)vt, ot, lse);
   return hipGetLastError();
 }
 

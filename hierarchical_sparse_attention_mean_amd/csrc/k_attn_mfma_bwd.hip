@@ -48,112 +48,159 @@ struct Flag {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
+// Query-stationary: a wavefront holds 32 query rows of Q~ and dO~ as B
+// operands; per 64-key tile, for each half of 32 keys, it forms S^T = K~ Q~^T
+// and dP^T = V~ dO~^T (lane = one query), dS^T = P^T o (dP^T - delta) in
+// registers, and accumulates dQ~^T += K~^T dS^T, the K~^T operand coming from
+// the row-major K~ tile by transposing reads.  8 wavefronts, 256 queries per
+// work-group; tiles in a ring of four LDS buffers filled three tiles ahead; LDS
+// operands streamed through a window of kDqWin fragments (as the forward).
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqBM = 32 * kDqWaves;
 constexpr int kDqBN = 64;
+constexpr int kDqBufs = 4;
+constexpr int kDqWin = 8;
 
 template <int D>
 struct DqTile {
-  static constexpr int WR = 2 * D;       // bytes per K~ / V~ row
-  static constexpr int WT = 2 * kDqBN;   // bytes per K~^T row
-  char k[kDqBN * WR];
-  char v[kDqBN * WR];
-  char kt[D * WT];
+  static constexpr int WR = 2 * D;   // bytes per K~ / V~ row
+  static constexpr int K = 0;
+  static constexpr int V = kDqBN * WR;
+  static constexpr int BYTES = 2 * kDqBN * WR;
 };
 
 template <int D>
 __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, int BH, const uint16_t *__restrict__ qt,
                                                                const uint16_t *__restrict__ kt,
                                                                const uint16_t *__restrict__ vt,
-                                                               const uint16_t *__restrict__ ktt,
                                                                const uint16_t *__restrict__ dotb,
                                                                const float *__restrict__ rows,
                                                                float *__restrict__ dqt) {
-  using Tile = DqTile<D>;
+  using T = DqTile<D>;
   constexpr int KC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) Tile buf[2];
+  constexpr int NA = 2 * KC;          // S^T / dP^T fragments per 32-key half (K~, V~ alternating)
+  constexpr int NH = NA + 2 * DB;     // ... plus the dQ fragments (K~^T) of the half
+  constexpr int NF = 2 * NH;          // fragments per tile
+  constexpr int KBLK = kDqBN * T::WR / 1024 / kDqWaves;   // 1 KB fill blocks per wavefront, K~ and V~ each
+  static_assert(KBLK * 1024 * kDqWaves == kDqBN * T::WR, "fill blocks");
+  constexpr int kFillOps = 2 * KBLK;
+  __shared__ __attribute__((aligned(1024))) char lds[kDqBufs * T::BYTES];
   const int nqb = (S + kDqBM - 1) / kDqBM;
   const int h = blockIdx.x % BH;
   const int qb = nqb - 1 - blockIdx.x / BH;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
-  const int q0 = qb * kDqBM, qw = q0 + 32 * w, qi = qw + ln;
-  const long long hbS = (long long)h * S;    // LSE, delta, dQ~: S rows per head
-  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~: Sv rows per head (rows S..Sv-1 zero)
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q0 = qb * kDqBM, qw = q0 + 32 * wu, qi = qw + ln;
+  const long long hbS = (long long)h * S;    // dQ~: S rows per head
+  const long long hbV = (long long)h * Sv;   // Q~, K~, V~, dO~, row pairs: Sv rows per head (rows S..Sv-1 zero)
   const char *kh = reinterpret_cast<const char *>(kt + hbV * D);
   const char *vh = reinterpret_cast<const char *>(vt + hbV * D);
-  const char *kth = reinterpret_cast<const char *>(ktt + (long long)h * D * Sv);
+  const unsigned lbase = tiles::lds_addr(lds);
 
-  // key tiles start below S and are 64 rows: they never pass the padded Sv rows
-  auto fill = [&](Tile &t, int k0) {
-    tiles::dma_tile<Tile::WR, kDqBN, kDqThreads>(t.k, kh + (long long)k0 * Tile::WR, Tile::WR, kDqBN - 1);
-    tiles::dma_tile<Tile::WR, kDqBN, kDqThreads>(t.v, vh + (long long)k0 * Tile::WR, Tile::WR, kDqBN - 1);
-    tiles::dma_tile<Tile::WT, D, kDqThreads>(t.kt, kth + 2LL * k0, 2LL * Sv, D - 1);
+  // fills: key tiles start below S and are 64 rows, so they never pass the Sv rows
+  unsigned vo[KBLK];
+#pragma unroll
+  for (int i = 0; i < KBLK; ++i) vo[i] = tiles::dma_voff<T::WR>(wu + i * kDqWaves, T::WR);
+  auto fill = [&](int jb, int k0) {
+    const unsigned m = lbase + jb * T::BYTES;
+#pragma unroll
+    for (int i = 0; i < KBLK; ++i) {
+      const unsigned blk = 1024u * (wu + i * kDqWaves);
+      tiles::lds_load_s<16>(kh + (long long)k0 * T::WR, vo[i], m + T::K + blk);
+      tiles::lds_load_s<16>(vh + (long long)k0 * T::WR, vo[i], m + T::V + blk);
+    }
+  };
+  // fragment j of a tile (half kb = j / NH, r = j % NH): r < NA: K~ (r even) or
+  // V~ (r odd) rows 32 kb + ln, chunk 2 (r/2) + hf; r >= NA: K~^T d rows
+  // 32 b + ln over the 16 keys of chunk 2 kb + cc (r - NA = cc DB + b)
+  int oq[KC], otr[DB][2];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) oq[c] = tiles::tile_off<T::WR>(ln, 2 * c + hf);
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    otr[b][0] = tiles::tr_off<T::WR>(0, 32 * b);
+    otr[b][1] = tiles::tr_off<T::WR>(8, 32 * b);
+  }
+  auto frag = [&](const char *buf, int j) -> bf16x8 {
+    const int kb = j / NH, r = j % NH;
+    if (r < NA) return tiles::lds_frag(buf + ((r & 1) ? T::V : T::K) + 32 * kb * T::WR, oq[r >> 1]);
+    const int cc = (r - NA) / DB, b = (r - NA) % DB;
+    return tiles::tr_frag(buf + T::K + 16 * (2 * kb + cc) * T::WR, otr[b][0], otr[b][1]);
   };
 
   bf16x8 qf[KC], gf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    if (qi < Sv) {
-      qf[c] = *reinterpret_cast<const bf16x8 *>(qt + (hbV + qi) * D + 16 * c + 8 * hf);
-      gf[c] = *reinterpret_cast<const bf16x8 *>(dotb + (hbV + qi) * D + 16 * c + 8 * hf);
-    } else {
-      qf[c] = (bf16x8){};
-      gf[c] = (bf16x8){};
-    }
+    qf[c] = (qi < Sv) ? *reinterpret_cast<const bf16x8 *>(qt + (hbV + qi) * D + 16 * c + 8 * hf) : (bf16x8){};
+    gf[c] = (qi < Sv) ? *reinterpret_cast<const bf16x8 *>(dotb + (hbV + qi) * D + 16 * c + 8 * hf) : (bf16x8){};
   }
-  const float c2 = kLog2e / sqrtf((float)D);
   // (LSE log2(e), delta) of this lane's query (zero on the padding rows)
   const float2 rq = qi < Sv ? *reinterpret_cast<const float2 *>(rows + 2 * (hbV + qi)) : make_float2(0.f, 0.f);
   const float lse2 = rq.x, dl = rq.y;
+  tiles::dma_wait();   // here, not inside the loop (see the forward)
+  const float c2 = kLog2e / sqrtf((float)D);
   f32x16 acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
 
   const int kend = min(S, q0 + kDqBM);
   const int nt = (kend + kDqBN - 1) / kDqBN;
-  fill(buf[0], 0);
-  tiles::dma_wait();
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
+  const int klast = (nt - 1) * kDqBN;
+  fill(0, 0);
+  fill(1, min(kDqBN, klast));
+  fill(2, min(2 * kDqBN, klast));
+  tiles::wait_fills_barrier<kFillOps>();   // tiles 0 and 1 landed
+  bf16x8 win[kDqWin];
+#pragma unroll
+  for (int j = 0; j < kDqWin; ++j) win[j] = frag(lds, j);
+
+  auto iteration = [&](int t, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
     const int k0 = t * kDqBN;
-    if (t + 1 < nt) fill(buf[(t + 1) & 1], k0 + kDqBN);
-    const Tile &cur = buf[t & 1];
-    if (k0 <= qw + 31) {   // otherwise the tile is in this wavefront's future
-      f32x16 st[2], dp[2];
+    fill((t + 3) & (kDqBufs - 1), min(k0 + 3 * kDqBN, klast));   // past the end: a repeat of the last tile
+    const char *cur = lds + (t & (kDqBufs - 1)) * T::BYTES;
+    const char *nxt = lds + ((t + 1) & (kDqBufs - 1)) * T::BYTES;
+    auto next = [&](int j) {   // the window moves on (into the next tile near the end)
+      win[j % kDqWin] = (j + kDqWin < NF) ? frag(cur, j + kDqWin) : frag(nxt, j + kDqWin - NF);
+      __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = (f32x16){};
-        dp[kb] = (f32x16){};
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 st = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const int off = tiles::tile_off<Tile::WR>(32 * kb + ln, 2 * c + hf);
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.k, off), qf[c], st[kb], 0, 0, 0);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tiles::lds_frag(cur.v, off), gf[c], dp[kb], 0, 0, 0);
-        }
+      for (int c = 0; c < KC; ++c) {
+        const int j = kb * NH + 2 * c;
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(win[j % kDqWin], qf[c], st, 0, 0, 0);
+        next(j);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(win[(j + 1) % kDqWin], gf[c], dp, 0, 0, 0);
+        next(j + 1);
       }
-      const bool diag = k0 + kDqBN - 1 > qw;   // causal mask (also masks the zero padding keys)
-      bf16x8 dsf[4];
+      bf16x8 dsf[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kb = c >> 1, i = 8 * (c & 1) + j;
+      for (int i = 0; i < 16; ++i) {
+        float pj = __builtin_amdgcn_exp2f(fmaf(st[i], c2, -lse2));
+        if constexpr (MASK) {
           const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          float pj = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c2, -lse2));
-          if (diag && key > qi) pj = 0.f;
-          dsf[c][j] = (__bf16)(pj * (dp[kb][i] - dl));
+          if (key > qi) pj = 0.f;
         }
+        dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dl));
+      }
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int b = 0; b < DB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tiles::lds_frag(cur.kt, tiles::tile_off<Tile::WT>(32 * b + ln, 2 * c + hf)), dsf[c], acc[b], 0, 0, 0);
+      for (int r = 0; r < 2 * DB; ++r) {   // dQ~^T += K~^T dS^T over the half's two 16-key chunks
+        const int j = kb * NH + NA + r;
+        acc[r % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(win[j % kDqWin], dsf[r / DB], acc[r % DB], 0, 0, 0);
+        next(j);
+      }
     }
-    tiles::dma_wait();
-    __syncthreads();
-  }
+    static_assert(kDqWin <= NA, "the reads kept in flight are single reads");
+    tiles::wait_fills_barrier_keep<kFillOps, kDqWin>();   // tile t+2 landed; the window's reads (tile t+1) stay in flight
+  };
+  const int nu = max(0, nt - kDqBM / kDqBN);   // tiles before the block's first query: no mask
+  for (int t = 0; t < nu; ++t) iteration(t, Flag<false>{});
+  for (int t = nu; t < nt; ++t) iteration(t, Flag<true>{});
+  tiles::dma_wait();   // the fills past the last tile, before the work-group exits
+
   if (qi >= S) return;
   const float scale = 1.f / sqrtf((float)D);
   float *orow = dqt + (hbS + qi) * D;
@@ -405,15 +452,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
 }  // namespace
 
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
-                                const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *rows, float *dqt, float *dkt, float *dvt, int part, hipStream_t st) {
+                                const void *dotb, const float *rows, float *dqt, float *dkt, float *dvt, int part,
+                                hipStream_t st) {
   const uint16_t *q = (const uint16_t *)qt, *k = (const uint16_t *)kt, *v = (const uint16_t *)vt;
-  const uint16_t *qT = (const uint16_t *)qtt, *kT = (const uint16_t *)ktt;
-  const uint16_t *g = (const uint16_t *)dotb, *gT = (const uint16_t *)dott;
+  const uint16_t *g = (const uint16_t *)dotb;
   dim3 gq(((S + kDqBM - 1) / kDqBM) * BH), gk(((S + kKvBK - 1) / kKvBK) * BH);
   if (part == 0) {   // dQ~
-    if (d == 128) k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
-    else k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, kT, g, rows, dqt);
+    if (d == 128) k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dqt);
+    else k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dqt);
   } else {           // dK~, dV~
     if (d == 128) k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);
     else k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);

@@ -14,10 +14,9 @@
 //   k_compact_gather  tile offset = sum of the earlier tiles' counts; block scan
 //                     inside the tile; writes the slot map (-1 for unselected
 //                     entries), the sorted flat coordinates, and copies the rows
-//                     of Q~, K~, V~ into place; in bf16 mode also their
-//                     transposes [d][Sv] with columns in the perm16 order the
-//                     MFMA kernels read (attn_tiles.h).
-#include "attn_tiles.h"
+//                     of Q~, K~, V~ into place (head stride Sv = S rounded up to
+//                     a multiple of 64, rows S..Sv-1 zero).
+#include "lh_internal.h"
 
 namespace lh {
 
@@ -65,14 +64,10 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
                                                             FwdWs w, const uint8_t *__restrict__ flags,
                                                             const int *__restrict__ tilecount, int *__restrict__ slot,
                                                             int *__restrict__ coords, T *__restrict__ qt,
-                                                            T *__restrict__ kt, T *__restrict__ vt,
-                                                            T *__restrict__ vtt, T *__restrict__ qtt,
-                                                            T *__restrict__ ktt) {
+                                                            T *__restrict__ kt, T *__restrict__ vt) {
   __shared__ int red[kThreads / 64];
   __shared__ int scan[kThreads];
   __shared__ int lflat[kCompactTile * 2];     // flat indices of this tile's slots (spills to global if more)
-  // bf16 only: rows of the current batch of 64 slots, for the transposed copies
-  __shared__ T stage[3][sizeof(T) == 2 ? 64 : 1][D + 2];
   const int h = blockIdx.y;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
@@ -136,80 +131,40 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
   const int j = tid % CH;
   const int rr = tid / CH;
   const long long hS = (long long)h * s.Sv;   // gathered rows: head stride Sv
-  for (int b0 = 0; b0 < ntot; b0 += 64) {
-    for (int r = rr; r < 64 && b0 + r < ntot; r += RPI) {
-      const int mm = b0 + r;
-      const int f = (mm < kCompactTile * 2) ? lflat[mm] : co[m0 + mm];
-      int l = 0;
-      while (l + 1 < s.L && f >= s.off[l + 1]) ++l;
-      const int i = f - s.off[l];
-      const T *sq, *sk, *sv;
-      if (l == 0) {
-        const long long base = ((long long)h * s.N + i) * D;
-        sq = q + base;
-        sk = k + base;
-        sv = v + base;
-      } else {
-        const long long base = ((long long)h * s.n[l] + i) * D;
-        sq = reinterpret_cast<const T *>(ws + w.lev[l][0]) + base;
-        sk = reinterpret_cast<const T *>(ws + w.lev[l][1]) + base;
-        sv = reinterpret_cast<const T *>(ws + w.lev[l][2]) + base;
-      }
-      const long long dst = (hS + m0 + mm) * D + j * 8;
-      if constexpr (sizeof(T) == 2) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(sq + j * 8);
-        const uint4 b = *reinterpret_cast<const uint4 *>(sk + j * 8);
-        const uint4 c = *reinterpret_cast<const uint4 *>(sv + j * 8);
-        *reinterpret_cast<uint4 *>(qt + dst) = a;
-        *reinterpret_cast<uint4 *>(kt + dst) = b;
-        *reinterpret_cast<uint4 *>(vt + dst) = c;
-        const T *ca = reinterpret_cast<const T *>(&a);
-        const T *cb = reinterpret_cast<const T *>(&b);
-        const T *cv = reinterpret_cast<const T *>(&c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          stage[0][r][j * 8 + e] = ca[e];
-          stage[1][r][j * 8 + e] = cb[e];
-          stage[2][r][j * 8 + e] = cv[e];
-        }
-      } else {
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const float4 a = *reinterpret_cast<const float4 *>(sq + j * 8 + hlf * 4);
-          const float4 b = *reinterpret_cast<const float4 *>(sk + j * 8 + hlf * 4);
-          const float4 c = *reinterpret_cast<const float4 *>(sv + j * 8 + hlf * 4);
-          *reinterpret_cast<float4 *>(qt + dst + hlf * 4) = a;
-          *reinterpret_cast<float4 *>(kt + dst + hlf * 4) = b;
-          *reinterpret_cast<float4 *>(vt + dst + hlf * 4) = c;
-        }
-      }
+  for (int mm = rr; mm < ntot; mm += RPI) {
+    const int f = (mm < kCompactTile * 2) ? lflat[mm] : co[m0 + mm];
+    int l = 0;
+    while (l + 1 < s.L && f >= s.off[l + 1]) ++l;
+    const int i = f - s.off[l];
+    const T *sq, *sk, *sv;
+    if (l == 0) {
+      const long long base = ((long long)h * s.N + i) * D;
+      sq = q + base;
+      sk = k + base;
+      sv = v + base;
+    } else {
+      const long long base = ((long long)h * s.n[l] + i) * D;
+      sq = reinterpret_cast<const T *>(ws + w.lev[l][0]) + base;
+      sk = reinterpret_cast<const T *>(ws + w.lev[l][1]) + base;
+      sv = reinterpret_cast<const T *>(ws + w.lev[l][2]) + base;
     }
+    const long long dst = (hS + m0 + mm) * D + j * 8;
     if constexpr (sizeof(T) == 2) {
-      // transposed copies: row dd of X~^T holds column dd of X~, for this batch of slots
-      __syncthreads();
-      const int nb = min(64, ntot - b0);
-      for (int idx = tid; idx < D * 64; idx += kThreads) {
-        const int dd = idx / 64;
-        const int c = idx % 64;
-        if (c < nb) {
-          const long long o = ((long long)h * D + dd) * s.Sv + tiles::perm16(m0 + b0 + c);
-          qtt[o] = stage[0][c][dd];
-          ktt[o] = stage[1][c][dd];
-          vtt[o] = stage[2][c][dd];
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if constexpr (sizeof(T) == 2) {
-    // zero the padding columns S..Sv-1 of the transposed copies (read as masked keys)
-    if (tile == s.ntile - 1) {
-      const int pad = s.Sv - s.S;
-      for (int idx = tid; idx < D * pad; idx += kThreads) {
-        const long long o = ((long long)h * D + idx / pad) * s.Sv + tiles::perm16(s.S + idx % pad);
-        qtt[o] = 0;
-        ktt[o] = 0;
-        vtt[o] = 0;
+      const uint4 a = *reinterpret_cast<const uint4 *>(sq + j * 8);
+      const uint4 b = *reinterpret_cast<const uint4 *>(sk + j * 8);
+      const uint4 c = *reinterpret_cast<const uint4 *>(sv + j * 8);
+      *reinterpret_cast<uint4 *>(qt + dst) = a;
+      *reinterpret_cast<uint4 *>(kt + dst) = b;
+      *reinterpret_cast<uint4 *>(vt + dst) = c;
+    } else {
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const float4 a = *reinterpret_cast<const float4 *>(sq + j * 8 + hlf * 4);
+        const float4 b = *reinterpret_cast<const float4 *>(sk + j * 8 + hlf * 4);
+        const float4 c = *reinterpret_cast<const float4 *>(sv + j * 8 + hlf * 4);
+        *reinterpret_cast<float4 *>(qt + dst + hlf * 4) = a;
+        *reinterpret_cast<float4 *>(kt + dst + hlf * 4) = b;
+        *reinterpret_cast<float4 *>(vt + dst + hlf * 4) = c;
       }
     }
   }
@@ -229,15 +184,14 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
 
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                                  const FwdWs &w, const uint8_t *flags, int *slot, int *coords, void *qt,
-                                 void *kt, void *vt, void *vtt, void *qtt, void *ktt, hipStream_t st) {
+                                 void *kt, void *vt, hipStream_t st) {
   char *wsb = reinterpret_cast<char *>(ws);
   int *tc = reinterpret_cast<int *>(wsb + w.tilecount);
   dim3 grid(s.ntile, s.BH);
   k_compact_count<<<grid, kThreads, 0, st>>>(s, flags, tc);
 #define LH_GATHER(T, D)                                                                                         \
   k_compact_gather<T, D><<<grid, kThreads, 0, st>>>(s, (const T *)q, (const T *)k, (const T *)v, wsb, w, flags, \
-                                                    tc, slot, coords, (T *)qt, (T *)kt, (T *)vt, (T *)vtt, \
-                                                    (T *)qtt, (T *)ktt)
+                                                    tc, slot, coords, (T *)qt, (T *)kt, (T *)vt)
   if (s.io == LH_BF16) {
     if (s.d == 128) LH_GATHER(uint16_t, 128);
     else LH_GATHER(uint16_t, 64);

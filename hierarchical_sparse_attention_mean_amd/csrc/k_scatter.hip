@@ -18,7 +18,7 @@
 //   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m;
 //   k_pool_bwd     dX_t = sum_l [entry (l, floor(t/p^l)) selected] dX~_slot / p^l
 //                  for X in {Q, K, V} (gather adjoint fused with pool adjoint).
-#include "attn_tiles.h"
+#include "lh_internal.h"
 
 namespace lh {
 
@@ -81,19 +81,17 @@ __device__ __forceinline__ float4 ld4(const void *p, long long off, int dtype) {
 // columns of dO over the entry's scatter range (t ascending), then
 //   delta_m = sum_d dO~[m][d] * O~[m][d]   (the softmax-backward row term)
 // with dO~ as the attention backward will read it (bf16-rounded in bf16 mode).
-// fp32 mode writes dO~ in fp32 and delta; bf16 mode writes dO~ in bf16,
-// row-major and transposed ([d][Sv], perm16 column order, through an LDS stage
-// so the columns are written coalesced), and the per-row pair
+// fp32 mode writes dO~ in fp32 and delta; bf16 mode writes dO~ in bf16
+// (row-major, head stride Sv, zero rows S..Sv-1) and the per-row pair
 // (LSE log2(e), delta) that the MFMA backward loads with each query tile
-// (zeros on the padding rows S..Sv-1).
+// (zeros on the padding rows).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__restrict__ dout, int dout_dtype,
                                                      const int *__restrict__ coords, const float *__restrict__ ot,
                                                      float *__restrict__ dot32, uint16_t *__restrict__ dotb,
-                                                     uint16_t *__restrict__ dott, float *__restrict__ delta,
-                                                     const float *__restrict__ lse, float *__restrict__ rows) {
+                                                     float *__restrict__ delta, const float *__restrict__ lse,
+                                                     float *__restrict__ rows) {
   constexpr int DP = D / 4;
-  __shared__ uint16_t stage[BF16 ? 64 : 1][D + 2];
   const int h = blockIdx.y;
   const int m0 = blockIdx.x * 64;
   const int r = threadIdx.x >> 2;
@@ -125,12 +123,12 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   const long long row = ((long long)h * s.S + m) * D + part * DP;
   const long long rowv = ((long long)h * s.Sv + m) * D + part * DP;   // bf16 dO~: head stride Sv
   float dl = 0.f;
+  uint16_t hb[BF16 ? DP : 1];   // dO~ as the attention backward reads it (bf16 mode)
   if constexpr (BF16) {
 #pragma unroll
     for (int e = 0; e < DP; ++e) {
-      const uint16_t b = f32_to_bf16_rne(acc[e]);
-      acc[e] = bf16_to_f32(b);
-      stage[r][part * DP + e] = b;
+      hb[e] = f32_to_bf16_rne(acc[e]);
+      acc[e] = bf16_to_f32(hb[e]);
     }
   }
   if (active) {
@@ -150,10 +148,10 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
 #pragma unroll
       for (int e = 0; e < DP; e += 8) {
         uint4 w;
-        w.x = (unsigned)stage[r][part * DP + e] | ((unsigned)stage[r][part * DP + e + 1] << 16);
-        w.y = (unsigned)stage[r][part * DP + e + 2] | ((unsigned)stage[r][part * DP + e + 3] << 16);
-        w.z = (unsigned)stage[r][part * DP + e + 4] | ((unsigned)stage[r][part * DP + e + 5] << 16);
-        w.w = (unsigned)stage[r][part * DP + e + 6] | ((unsigned)stage[r][part * DP + e + 7] << 16);
+        w.x = (unsigned)hb[e] | ((unsigned)hb[e + 1] << 16);
+        w.y = (unsigned)hb[e + 2] | ((unsigned)hb[e + 3] << 16);
+        w.z = (unsigned)hb[e + 4] | ((unsigned)hb[e + 5] << 16);
+        w.w = (unsigned)hb[e + 6] | ((unsigned)hb[e + 7] << 16);
         *reinterpret_cast<uint4 *>(dotb + rowv + e) = w;
       }
     }
@@ -169,16 +167,6 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
 #pragma unroll
       for (int e = 0; e < DP; e += 4)
         *reinterpret_cast<float4 *>(dot32 + row + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-    }
-  }
-  if constexpr (BF16) {
-    __syncthreads();
-    // columns past S (up to the padded stride Sv) are written as zeros
-    const int nb = min(64, s.S - m0);
-    for (int idx = threadIdx.x; idx < D * 64; idx += 256) {
-      const int dd = idx / 64, c = idx % 64;
-      if (m0 + c < s.Sv)
-        dott[((long long)h * D + dd) * s.Sv + tiles::perm16(m0 + c)] = c < nb ? stage[c][dd] : (uint16_t)0;
     }
   }
 }
@@ -237,12 +225,12 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void
 }
 
 hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
-                              const float *lse, float *dot32, uint16_t *dotb, uint16_t *dott, float *delta,
-                              float *rows, hipStream_t st) {
+                              const float *lse, float *dot32, uint16_t *dotb, float *delta, float *rows,
+                              hipStream_t st) {
   // bf16 mode also writes the zero padding rows / columns up to Sv (a multiple of 64)
   dim3 grid((unsigned)(((s.io == LH_BF16 ? s.Sv : s.S) + 63) / 64), s.BH);
   const bool bf = s.io == LH_BF16;
-#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, dott, delta, lse, rows)
+#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, delta, lse, rows)
   if (s.d == 128) {
     if (bf) LH_SB(128, true);
     else LH_SB(128, false);

@@ -16,14 +16,14 @@
 namespace lh {
 hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st);
-hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, int vstride, const void *qt, const void *kt, const void *vtt,
+hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st);
 hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 const float *ot, const float *lse, const float *dot, float *delta, float *dqt,
                                 float *dkt, float *dvt, int part, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
-                                const void *qtt, const void *ktt, const void *dotb, const void *dott,
-                                const float *rows, float *dqt, float *dkt, float *dvt, int part, hipStream_t st);
+                                const void *dotb, const float *rows, float *dqt, float *dkt, float *dvt, int part,
+                                hipStream_t st);
 }  // namespace lh
 
 namespace {
@@ -167,9 +167,6 @@ void saved_layout(const lh::Shape &s, lh_saved_layout_t *o) {
   o->qt = take(es * BH * Sv * d);
   o->kt = take(es * BH * Sv * d);
   o->vt = take(es * BH * Sv * d);
-  o->vtt = take(es * BH * (size_t)s.Sv * d);
-  o->qtt = take(es * BH * (size_t)s.Sv * d);
-  o->ktt = take(es * BH * (size_t)s.Sv * d);
   o->ot = take(4 * BH * S * d);
   o->lse = take(4 * BH * S);
   o->total = cur;
@@ -212,7 +209,6 @@ void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
   const bool bf = s.io == LH_BF16;
   w->dot = take(bf ? 0 : 4 * BH * S * d);
   w->dotb = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
-  w->dott = take(bf ? 2 * BH * (size_t)s.Sv * d : 0);
   w->delta = take(bf ? 0 : 4 * BH * S);
   w->rows = take(bf ? 8 * BH * (size_t)s.Sv : 0);
   w->dqt = take(4 * BH * S * d);
@@ -318,7 +314,7 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   {
     Span sp(LH_STAGE_GATHER, hs);
     if ((st = hip_check(lh::launch_compact_gather(s, q, k, v, ws, fw, flags, slot, coords, sv + sl.qt, sv + sl.kt,
-                                                  sv + sl.vt, sv + sl.vtt, sv + sl.qtt, sv + sl.ktt, hs),
+                                                  sv + sl.vt, hs),
                         "compact_gather")) != LH_OK)
       return st;
   }
@@ -327,7 +323,7 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
     Span sp(LH_STAGE_ATTN_FWD, hs);
     hipError_t e;
     if (s.io == LH_BF16)
-      e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vtt, ot, lse, hs);
+      e = lh::launch_attn_fwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
     else
       e = lh::launch_attn_fwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, hs);
     if ((st = hip_check(e, "attention")) != LH_OK) return st;
@@ -370,7 +366,6 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   const float *lse = reinterpret_cast<const float *>(sv + sl.lse);
   float *dot = reinterpret_cast<float *>(wb + bw.dot);
   uint16_t *dotb = reinterpret_cast<uint16_t *>(wb + bw.dotb);
-  uint16_t *dott = reinterpret_cast<uint16_t *>(wb + bw.dott);
   float *delta = reinterpret_cast<float *>(wb + bw.delta);
   float *rows = reinterpret_cast<float *>(wb + bw.rows);
   float *dqt = reinterpret_cast<float *>(wb + bw.dqt);
@@ -383,7 +378,7 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   // adjoint of the scatter: dO~ (and delta = rowsum(dO~ * O~))
   {
     Span sp(LH_STAGE_SCATTER_BWD, hs);
-    if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, dott, delta, rows, hs),
+    if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, delta, rows, hs),
                         "scatter_bwd")) != LH_OK)
       return st;
   }
@@ -392,8 +387,8 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
     Span sp(part == 0 ? LH_STAGE_ATTN_BWD_DQ : LH_STAGE_ATTN_BWD_DKDV, hs);
     hipError_t e;
     if (s.io == LH_BF16)
-      e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, sv + sl.qtt, sv + sl.ktt,
-                                   dotb, dott, rows, dqt, dkt, dvt, part, hs);
+      e = lh::launch_attn_bwd_mfma(s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, dotb, rows, dqt, dkt,
+                                   dvt, part, hs);
     else
       e = lh::launch_attn_bwd_valu(s.io, s.d, s.BH, s.S, s.Sv, sv + sl.qt, sv + sl.kt, sv + sl.vt, ot, lse, dot, delta,
                                    dqt, dkt, dvt, part, hs);
@@ -409,19 +404,19 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   return LH_OK;
 }
 
-lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse, int BH, int64_t S,
+lh_status lh_attention_forward(const void *q, const void *k, const void *v, float *o, float *lse, int BH, int64_t S,
                                int d, lh_dtype io, void *stream) {
   if (BH < 1 || S < 1) return fail(LH_EINVAL, "BH and S must be >= 1");
   if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
   if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
   if (S * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
-    return fail(LH_EINVAL, "q, k, vt, o must be non-NULL and 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(LH_EINVAL, "q, k, v, o must be non-NULL and 16-byte aligned");
   if (lse && ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be 4-byte aligned");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)S, (int)((S + 63) & ~63), q, k, vt, o, lse, hs);
-  else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, (int)S, q, k, vt, o, lse, hs);
+  if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)S, q, k, v, o, lse, hs);
+  else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, (int)S, q, k, v, o, lse, hs);
   return hip_check(e, "attention");
 }
 

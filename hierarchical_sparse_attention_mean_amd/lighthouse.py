@@ -38,8 +38,7 @@ class LighthouseError(RuntimeError):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse",
-                          "total")] + \
+                ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "ot", "lse", "total")] + \
                [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S", "Sv")]
 
 
@@ -162,8 +161,8 @@ def lh_backward(q, k, v, dout, dout_dtype, saved, saved_bytes, dq, dk, dv, grad_
                             topk, dtype_code(io), _ptr(ws), ws_bytes, _stream(stream))
 
 
-def lh_attention_forward(q, k, vt, o, lse, BH, S, d, io, stream=None):
-    return _lib.lh_attention_forward(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(lse), BH, S, d, dtype_code(io),
+def lh_attention_forward(q, k, v, o, lse, BH, S, d, io, stream=None):
+    return _lib.lh_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, S, d, dtype_code(io),
                                      _stream(stream))
 
 
@@ -239,7 +238,6 @@ def saved_view(saved, plan, name):
         "scores": (torch.float32, (BH, 2, P)), "flags": (torch.uint8, (BH, P)), "slot": (torch.int32, (BH, P)),
         "coords": (torch.int32, (BH, S)), "qt": (io, (BH, lay["Sv"], d)), "kt": (io, (BH, lay["Sv"], d)),
         "vt": (io, (BH, lay["Sv"], d)),
-        "vtt": (io, (BH, d, lay["Sv"])), "qtt": (io, (BH, d, lay["Sv"])), "ktt": (io, (BH, d, lay["Sv"])),
         "ot": (torch.float32, (BH, S, d)), "lse": (torch.float32, (BH, S)),
     }[name]
     dt, shape = spec

@@ -66,15 +66,10 @@ typedef struct lh_saved_layout_t {
   size_t flags;    /* uint8 [BH][P]     1 = entry is in the index set I */
   size_t slot;     /* int32 [BH][P]     position in the sub-sequence, -1 if not selected */
   size_t coords;   /* int32 [BH][S]     flat pyramid index of the entry at each slot */
-  size_t qt;       /* io    [BH][Sv][d] gathered Q~ (topological order); rows S..Sv-1 zero */
+  size_t qt;       /* io    [BH][Sv][d] gathered Q~ (topological order); head stride Sv = S
+                            rounded up to a multiple of 64, rows S..Sv-1 zero */
   size_t kt;       /* io    [BH][Sv][d] gathered K~; rows S..Sv-1 zero */
   size_t vt;       /* io    [BH][Sv][d] gathered V~; rows S..Sv-1 zero */
-  size_t vtt;      /* io    [BH][d][Sv] V~ transposed, row stride Sv = S rounded up to a multiple
-                            of 64; element m of a row sits at column perm16(m) = m with bits 2
-                            and 3 swapped; columns of m >= S zero (operand layout of the bf16
-                            MFMA kernels; LH_BF16 only) */
-  size_t qtt;      /* io    [BH][d][Sv] Q~ transposed, same layout (LH_BF16 only) */
-  size_t ktt;      /* io    [BH][d][Sv] K~ transposed, same layout (LH_BF16 only) */
   size_t ot;       /* fp32  [BH][S][d]  sub-sequence attention output O~ */
   size_t lse;      /* fp32  [BH][S]     natural-log log-sum-exp of each O~ row's logits */
   size_t total;    /* bytes needed */
@@ -82,7 +77,7 @@ typedef struct lh_saved_layout_t {
   int64_t E;       /* candidate (non-coarsest) entries per head */
   int64_t Bsel;    /* selected candidates per head */
   int64_t S;       /* gathered length per head */
-  int64_t Sv;      /* row stride of vtt, qtt, ktt: S rounded up to a multiple of 64 */
+  int64_t Sv;      /* rows per head of qt, kt, vt: S rounded up to a multiple of 64 */
 } lh_saved_layout_t;
 
 /* Host-only.  Validates the shape and returns S and the byte sizes the caller
@@ -123,14 +118,9 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
 /* Dense causal softmax attention, softmax(Q K^T / sqrt(d) + causal) V, on given
  * [BH,S,d] tensors (Sec. 3.1, Eq. 1): the kernel of stage (iii), exposed for the
  * dense baseline at S = N.
- *   q, k   : [BH][S][d] dtype `io`.
- *   vt     : LH_BF16: V transposed, [BH][d][Sv] with row stride Sv = S rounded up
- *            to a multiple of 64, element m of a row at column perm16(m) (m with
- *            bits 2 and 3 swapped) and the columns of m >= S zero (the bf16 MFMA
- *            kernel's operand layout);
- *            LH_F32: V itself, [BH][S][d].
- *   o      : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
-lh_status lh_attention_forward(const void *q, const void *k, const void *vt, float *o, float *lse,
+ *   q, k, v : [BH][S][d] dtype `io` (read only).
+ *   o       : [BH][S][d] fp32.   lse: [BH][S] fp32 (may be NULL).  */
+lh_status lh_attention_forward(const void *q, const void *k, const void *v, float *o, float *lse,
                                int BH, int64_t S, int d, lh_dtype io, void *stream);
 
 /* Stages of lh_forward / lh_backward, for stage timing. */

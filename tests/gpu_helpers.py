@@ -10,13 +10,6 @@ import oracle as orc
 from hierarchical_sparse_attention_mean_amd import synth
 
 
-def perm16(m):
-    """Column position of element m in the library's transposed copies: bits 2
-    and 3 of the index swapped (the order its MFMA kernels read)."""
-    m = np.asarray(m)
-    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1)
-
-
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -67,9 +60,6 @@ def gpu_head(lh, run: dict, h: int) -> dict:
     for n in ("qt", "kt", "vt"):   # rows S..Sv-1 are padding (zero)
         full = bf16_tensor_to_f64(lh.saved_view(saved, plan, n)[h])
         out[n], out[n + "_pad"] = full[:S], full[S:]
-    for n in ("vtt", "qtt", "ktt"):   # back to natural column order
-        t = bf16_tensor_to_f64(lh.saved_view(saved, plan, n)[h])
-        out[n] = t[:, perm16(np.arange(t.shape[1]))]
     out["ot32"] = lh.saved_view(saved, plan, "ot")[h].cpu().numpy()
     out["lse"] = lh.saved_view(saved, plan, "lse")[h].cpu().numpy().astype(np.float64)
     o = run["o"]

@@ -35,16 +35,18 @@ def test_query_matches_closed_form(lh, B, H, N, d, L, p, k, io):
     assert lay["Sv"] == (S + 63) // 64 * 64
     es = 2 if io == "bf16" else 4
     BH = B * H
-    order = ["scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse"]
+    order = ["scores", "flags", "slot", "coords", "qt", "kt", "vt", "ot", "lse"]
     need = {"scores": 8 * BH * lay["P"], "flags": BH * lay["P"], "slot": 4 * BH * lay["P"], "coords": 4 * BH * S,
-            "qt": es * BH * lay["Sv"] * d, "kt": es * BH * lay["Sv"] * d, "vt": es * BH * lay["Sv"] * d, "vtt": es * BH * lay["Sv"] * d,
-            "qtt": es * BH * lay["Sv"] * d, "ktt": es * BH * lay["Sv"] * d,
+            "qt": es * BH * lay["Sv"] * d, "kt": es * BH * lay["Sv"] * d, "vt": es * BH * lay["Sv"] * d,
             "ot": 4 * BH * S * d, "lse": 4 * BH * S}
     for a, b in zip(order, order[1:] + ["total"]):
         assert lay[a] % 256 == 0
         assert lay[b] - lay[a] >= need[a]           # arrays do not overlap
     assert saved == lay["total"]
-    assert fws > 0 and bws >= 4 * BH * S * d * 4
+    # backward workspace: dQ~, dK~, dV~ in fp32, plus dO~ (fp32 in fp32 mode; bf16 rows padded to Sv and the
+    # (LSE log2 e, delta) row pairs in bf16 mode)
+    need_bws = 3 * 4 * BH * S * d + (4 * BH * S * d if io == "f32" else 2 * BH * lay["Sv"] * d + 8 * BH * lay["Sv"])
+    assert fws > 0 and bws >= need_bws
 
 
 def test_page_example_S_through_abi(lh):

@@ -69,11 +69,8 @@ def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True,
         assert np.array_equal(got[base], ref[base]), f"{name}: level-0 rows not bit-exact"
         rel = 2.0 ** -8 if dt == "bf16" else 2e-6
         assert np.all(np.abs(got[~base] - ref[~base]) <= rel * np.abs(ref[~base]) + 1e-6), f"{name} pooled rows"
-    if dt == "bf16":
-        Sv = g["vtt"].shape[1]
-        for tn, n in (("vtt", "vt"), ("qtt", "qt"), ("ktt", "kt")):
-            assert np.array_equal(g[tn][:, :S].T, g[n]), f"{tn}: transposed copy differs"
-            assert not np.any(g[tn][:, S:Sv]) and not np.any(g[n + "_pad"]), f"{n}: padding not zero"
+    for n in ("qt", "kt", "vt"):
+        assert not np.any(g[n + "_pad"]), f"{n}: padding rows not zero"
     # ---- attention on the GPU's own gathered rows
     if full_attention:
         ot_ref, lse_ref = orc.attend(g["qt"], g["kt"], g["vt"])
@@ -188,7 +185,7 @@ def test_deterministic(lh):
     a = run_forward(lh, cfg, inp, out_dtype="bf16")
     b = run_forward(lh, cfg, inp, out_dtype="bf16")
     assert torch.equal(a["o"].view(torch.int16), b["o"].view(torch.int16))
-    for n in ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "vtt", "qtt", "ktt", "ot", "lse"):
+    for n in ("scores", "flags", "slot", "coords", "qt", "kt", "vt", "ot", "lse"):
         x = lh.saved_view(a["saved"], a["plan"], n)
         y = lh.saved_view(b["saved"], b["plan"], n)
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
