@@ -33,38 +33,77 @@ __device__ __forceinline__ float from_fixed(long long a) {
   return (float)((double)a * 2.3283064365386963e-10);   // * 2^-32, then fp32 round-to-nearest-even
 }
 
+constexpr int kMaxL = 8;   // levels supported (validated on the host)
+
+// One thread per 8 consecutive elements of an output row (16-byte stores).  The
+// slots of the entries that reach position t at each level are looked up
+// first, then their rows are read.  Fixed-point sum: sum over the levels of
+// RNE(x 2^32) as an integer, converted back with one rounding.  RNE(x 2^32) is
+// an integer that fp32 rintf gives exactly; while every |x| < 2^18 each term is
+// below 2^50 in magnitude and the sum of at most kMaxL of them is exact in
+// fp64, which is then the same integer as the int64 sum (and (double)int64
+// gives the same value): that path is taken unless some |x| >= 2^18, where the
+// int64 sum is formed instead.
 template <int D>
 __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict__ slot, const float *__restrict__ ot,
                                                  void *__restrict__ o, int o_dtype) {
-  constexpr int C4 = D / 4;   // float4 chunks per row
+  constexpr int C8 = D / 8;   // 8-element chunks per row
   const int h = blockIdx.y;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)s.N * C4) return;
-  const int t = (int)(idx / C4);
-  const int c = (int)(idx % C4);
+  if (idx >= (long long)s.N * C8) return;
+  const int t = (int)(idx / C8);
+  const int c = (int)(idx % C8);
   const int *sl = slot + (long long)h * s.P;
-  const float4 *ob = reinterpret_cast<const float4 *>(ot + (long long)h * s.S * D);
-  long long a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-  for (int l = 0; l < s.L; ++l) {
-    const int i = (t + 1) / s.pw[l] - 1;
-    if (i < 0) break;   // coarser levels start even later
-    const int m = sl[s.off[l] + i];
-    if (m < 0) continue;
-    const float4 x = ob[(long long)m * C4 + c];
-    a0 += to_fixed(x.x);
-    a1 += to_fixed(x.y);
-    a2 += to_fixed(x.z);
-    a3 += to_fixed(x.w);
+  const float *ob = ot + (long long)h * s.S * D + c * 8;
+  int m[kMaxL];
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l) {
+    m[l] = -1;
+    if (l < s.L) {
+      const int i = (t + 1) / s.pw[l] - 1;
+      if (i >= 0) m[l] = sl[s.off[l] + i];
+    }
   }
-  const float r0 = from_fixed(a0), r1 = from_fixed(a1), r2 = from_fixed(a2), r3 = from_fixed(a3);
-  const long long off = ((long long)h * s.N + t) * D + c * 4;
-  if (o_dtype == LH_BF16) {
-    uint2 w;
-    w.x = (unsigned)f32_to_bf16_rne(r0) | ((unsigned)f32_to_bf16_rne(r1) << 16);
-    w.y = (unsigned)f32_to_bf16_rne(r2) | ((unsigned)f32_to_bf16_rne(r3) << 16);
-    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(o) + off) = w;
+  double a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = 0.0;
+  bool big = false;
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l) {
+    if (m[l] < 0) continue;
+    const float4 x0 = *reinterpret_cast<const float4 *>(ob + (long long)m[l] * D);
+    const float4 x1 = *reinterpret_cast<const float4 *>(ob + (long long)m[l] * D + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      big |= !(fabsf(x[e]) < 262144.f);
+      a[e] += (double)rintf(x[e] * 4294967296.0f);
+    }
+  }
+  float r[8];
+  if (!big) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (float)(a[e] * 2.3283064365386963e-10);
   } else {
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(o) + off) = make_float4(r0, r1, r2, r3);
+    long long b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int l = 0; l < kMaxL; ++l) {
+      if (m[l] < 0) continue;
+      for (int e = 0; e < 8; ++e) b[e] += to_fixed(ob[(long long)m[l] * D + e]);
+    }
+    for (int e = 0; e < 8; ++e) r[e] = from_fixed(b[e]);
+  }
+  const long long off = ((long long)h * s.N + t) * D + c * 8;
+  if (o_dtype == LH_BF16) {
+    uint4 w;
+    w.x = (unsigned)f32_to_bf16_rne(r[0]) | ((unsigned)f32_to_bf16_rne(r[1]) << 16);
+    w.y = (unsigned)f32_to_bf16_rne(r[2]) | ((unsigned)f32_to_bf16_rne(r[3]) << 16);
+    w.z = (unsigned)f32_to_bf16_rne(r[4]) | ((unsigned)f32_to_bf16_rne(r[5]) << 16);
+    w.w = (unsigned)f32_to_bf16_rne(r[6]) | ((unsigned)f32_to_bf16_rne(r[7]) << 16);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(o) + off) = w;
+  } else {
+    float *of = reinterpret_cast<float *>(o) + off;
+    *reinterpret_cast<float4 *>(of) = make_float4(r[0], r[1], r[2], r[3]);
+    *reinterpret_cast<float4 *>(of + 4) = make_float4(r[4], r[5], r[6], r[7]);
   }
 }
 
@@ -171,53 +210,68 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   }
 }
 
+// One thread per 8 consecutive elements of a position's row of dQ, dK, dV
+// (16-byte stores); slots of the position's entries looked up first.
+// Arithmetic: per level in ascending order, acc = fma(dX~, 1/p^l, acc).
 template <int D>
 __global__ __launch_bounds__(256) void k_pool_bwd(Shape s, const int *__restrict__ slot, const float *__restrict__ dqt,
                                                   const float *__restrict__ dkt, const float *__restrict__ dvt,
                                                   void *__restrict__ dq, void *__restrict__ dk, void *__restrict__ dv,
                                                   int grad_dtype) {
-  constexpr int C4 = D / 4;
+  constexpr int C8 = D / 8;
   const int h = blockIdx.y;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)s.N * C4) return;
-  const int t = (int)(idx / C4);
-  const int c = (int)(idx % C4);
+  if (idx >= (long long)s.N * C8) return;
+  const int t = (int)(idx / C8);
+  const int c = (int)(idx % C8);
   const int *sl = slot + (long long)h * s.P;
   const long long hs = (long long)h * s.S;
-  float4 aq = make_float4(0.f, 0.f, 0.f, 0.f), ak = aq, av = aq;
-  for (int l = 0; l < s.L; ++l) {
-    const int m = sl[s.off[l] + t / s.pw[l]];
-    if (m < 0) continue;
+  int m[kMaxL];
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l) m[l] = (l < s.L) ? sl[s.off[l] + t / s.pw[l]] : -1;
+  float acc[3][8];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+  const float *src[3] = {dqt, dkt, dvt};
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l) {
+    if (m[l] < 0) continue;
     const float inv = 1.f / (float)s.pw[l];
-    const long long ro = (hs + m) * D + c * 4;
-    const float4 x = *reinterpret_cast<const float4 *>(dqt + ro);
-    const float4 y = *reinterpret_cast<const float4 *>(dkt + ro);
-    const float4 z = *reinterpret_cast<const float4 *>(dvt + ro);
-    aq.x = fmaf(x.x, inv, aq.x); aq.y = fmaf(x.y, inv, aq.y); aq.z = fmaf(x.z, inv, aq.z); aq.w = fmaf(x.w, inv, aq.w);
-    ak.x = fmaf(y.x, inv, ak.x); ak.y = fmaf(y.y, inv, ak.y); ak.z = fmaf(y.z, inv, ak.z); ak.w = fmaf(y.w, inv, ak.w);
-    av.x = fmaf(z.x, inv, av.x); av.y = fmaf(z.y, inv, av.y); av.z = fmaf(z.z, inv, av.z); av.w = fmaf(z.w, inv, av.w);
-  }
-  const long long off = ((long long)h * s.N + t) * D + c * 4;
-  if (grad_dtype == LH_BF16) {
-    const float4 *src[3] = {&aq, &ak, &av};
-    void *dst[3] = {dq, dk, dv};
+    const long long ro = (hs + m[l]) * D + c * 8;
+#pragma unroll
     for (int u = 0; u < 3; ++u) {
-      uint2 w;
-      w.x = (unsigned)f32_to_bf16_rne(src[u]->x) | ((unsigned)f32_to_bf16_rne(src[u]->y) << 16);
-      w.y = (unsigned)f32_to_bf16_rne(src[u]->z) | ((unsigned)f32_to_bf16_rne(src[u]->w) << 16);
-      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(dst[u]) + off) = w;
+      const float4 x0 = *reinterpret_cast<const float4 *>(src[u] + ro);
+      const float4 x1 = *reinterpret_cast<const float4 *>(src[u] + ro + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = fmaf(x[e], inv, acc[u][e]);
     }
-  } else {
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(dq) + off) = aq;
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(dk) + off) = ak;
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(dv) + off) = av;
+  }
+  const long long off = ((long long)h * s.N + t) * D + c * 8;
+  void *dst[3] = {dq, dk, dv};
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    if (grad_dtype == LH_BF16) {
+      uint4 w;
+      w.x = (unsigned)f32_to_bf16_rne(acc[u][0]) | ((unsigned)f32_to_bf16_rne(acc[u][1]) << 16);
+      w.y = (unsigned)f32_to_bf16_rne(acc[u][2]) | ((unsigned)f32_to_bf16_rne(acc[u][3]) << 16);
+      w.z = (unsigned)f32_to_bf16_rne(acc[u][4]) | ((unsigned)f32_to_bf16_rne(acc[u][5]) << 16);
+      w.w = (unsigned)f32_to_bf16_rne(acc[u][6]) | ((unsigned)f32_to_bf16_rne(acc[u][7]) << 16);
+      *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(dst[u]) + off) = w;
+    } else {
+      float *of = reinterpret_cast<float *>(dst[u]) + off;
+      *reinterpret_cast<float4 *>(of) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+      *reinterpret_cast<float4 *>(of + 4) = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void *o, int o_dtype, hipStream_t st) {
-  const long long n = (long long)s.N * (s.d / 4);
+  const long long n = (long long)s.N * (s.d / 8);
   dim3 grid((unsigned)((n + 255) / 256), s.BH);
   if (s.d == 128) k_scatter<128><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);
   else k_scatter<64><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);
@@ -244,7 +298,7 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
 
 hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, const float *dkt, const float *dvt,
                            void *dq, void *dk, void *dv, int grad_dtype, hipStream_t st) {
-  const long long n = (long long)s.N * (s.d / 4);
+  const long long n = (long long)s.N * (s.d / 8);
   dim3 grid((unsigned)((n + 255) / 256), s.BH);
   if (s.d == 128) k_pool_bwd<128><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);
   else k_pool_bwd<64><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);

@@ -189,3 +189,21 @@ def test_deterministic(lh):
         x = lh.saved_view(a["saved"], a["plan"], n)
         y = lh.saved_view(b["saved"], b["plan"], n)
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
+
+
+def test_scatter_large_values(lh):
+    """Sub-sequence outputs of magnitude >= 2^18 make the scatter form its
+    fixed-point sums in int64 instead of fp64; the result stays bit-exact.
+    V is scaled by 2^20 on half of the positions, so both forms occur."""
+    cfg = synth.config("tiny")
+    inp = synth.make_inputs(cfg)
+    N, L, p = cfg["N"], cfg["L"], cfg["p"]
+    inp["v"] = inp["v"].copy()
+    inp["v"][..., N // 2:, :] *= 2.0 ** 20
+    run = run_forward(lh, cfg, inp)
+    for h in range(cfg["B"] * cfg["H"]):
+        g = gpu_head(lh, run, h)
+        big = np.abs(g["ot32"]) >= 2.0 ** 18
+        assert big.any() and (~big).any()
+        o_fx = orc.scatter_fixed(g["ot32"].astype(np.float64), g["coords"], N, L, p, "f32")
+        assert np.array_equal(o_fx, g["o"]), "scatter not bit-exact"
