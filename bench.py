@@ -226,19 +226,34 @@ def main() -> int:
              "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
     stream = torch.cuda.current_stream()
     if args.dense:
+        # the same attention kernels on the full sequence (S = N): dense causal attention forward and backward
+        q3, k3, v3, do3 = (x.reshape(BH, N, d) for x in (q, kk, v, do))
         od = torch.empty((BH, N, d), dtype=torch.float32, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lsed = torch.empty((BH, N), dtype=torch.float32, device=dev)
+        grads = [torch.empty((BH, N, d), dtype=torch.float32, device=dev) for _ in range(3)]
+        nb = lh.attention_backward_ws_bytes(BH, N, io)
+        wsd = torch.empty(nb, dtype=torch.uint8, device=dev)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        lh.lh_timing_begin()
         e0.record(stream)
-        st = lh.lh_attention_forward(q.reshape(BH, N, d), kk.reshape(BH, N, d), v.reshape(BH, N, d), od, None, BH, N,
-                                     d, io)
+        st = lh.lh_attention_forward(q3, k3, v3, od, lsed, BH, N, d, io)
         e1.record(stream)
+        st2 = lh.lh_attention_backward(q3, k3, v3, od, lsed, do3, *grads, BH, N, d, io, wsd, nb)
+        e2.record(stream)
         torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1)
-        extra["dense_attn_fwd_ms_at_S_eq_N"] = dms
-        extra["dense_attn_fwd_tflops"] = attention_flops(N, d, BH) / (dms * 1e-3) / 1e12
-        extra["lighthouse_fwd_speedup_vs_dense"] = dms / ms_fwd
-        log(f"[bench] dense causal attention at S=N: {dms:.1f} ms")
-        del od
+        st3, dstages = lh.lh_timing_end()
+        if st or st2 or st3:
+            raise lh.LighthouseError(st or st2 or st3, "dense attention")
+        fms, bms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+        extra["dense_attn_fwd_ms_at_S_eq_N"] = fms
+        extra["dense_attn_fwd_tflops"] = attention_flops(N, d, BH) / (fms * 1e-3) / 1e12
+        extra["dense_attn_bwd_ms_at_S_eq_N"] = bms
+        extra["dense_attn_bwd_tflops_executed"] = attention_flops(N, d, BH, 7) / (bms * 1e-3) / 1e12
+        extra["dense_attn_bwd_stage_ms"] = {n: dstages[n][0] for n in ("scatter_bwd", "attn_bwd_dq", "attn_bwd_dkdv")}
+        extra["lighthouse_fwd_speedup_vs_dense"] = fms / ms_fwd
+        extra["lighthouse_step_speedup_vs_dense"] = (fms + bms) / ms
+        log(f"[bench] dense causal attention at S=N: forward {fms:.1f} ms, backward {bms:.1f} ms")
+        del od, lsed, grads, wsd
 
     cpu = None
     if not args.no_cpu_baseline:

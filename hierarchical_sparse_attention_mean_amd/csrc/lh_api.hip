@@ -24,6 +24,8 @@ hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void
 hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, const void *kt, const void *vt,
                                 const void *dotb, const float *rows, float *dqt, float *dkt, float *dvt, int part,
                                 hipStream_t st);
+hipError_t launch_attn_rowstats(int d, int BH, int S, const void *dout, int dout_bf16, const float *o,
+                                const float *lse, float *pairs, float *delta, hipStream_t st);
 }  // namespace lh
 
 namespace {
@@ -418,6 +420,46 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *v, floa
   if (io == LH_BF16) e = lh::launch_attn_fwd_mfma(d, BH, (int)S, (int)S, q, k, v, o, lse, hs);
   else e = lh::launch_attn_fwd_valu(io, d, BH, (int)S, (int)S, q, k, v, o, lse, hs);
   return hip_check(e, "attention");
+}
+
+lh_status lh_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                                const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
+                                lh_dtype io, void *ws, size_t ws_bytes, void *stream) {
+  if (BH < 1 || S < 1) return fail(LH_EINVAL, "BH and S must be >= 1");
+  if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
+  if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
+  if (S * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
+  if (io == LH_BF16 && S % 64 != 0)
+    return fail(LH_EUNSUPPORTED, "LH_BF16 needs S to be a multiple of 64 (got %lld)", (long long)S);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout))
+    return fail(LH_EINVAL, "q, k, v, o, dout must be non-NULL and 16-byte aligned");
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(LH_EINVAL, "dq, dk, dv must be non-NULL and 16-byte aligned");
+  if (!lse || ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be non-NULL and 4-byte aligned");
+  if (!aligned16(ws)) return fail(LH_EINVAL, "ws must be non-NULL and 16-byte aligned");
+  const size_t need = (io == LH_BF16 ? 8 : 4) * (size_t)BH * (size_t)S;
+  if (ws_bytes < need) return fail(LH_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float *wsf = reinterpret_cast<float *>(ws);
+  lh_status st;
+  {
+    Span sp(LH_STAGE_SCATTER_BWD, hs);   // the row terms take the place of the scatter adjoint
+    if ((st = hip_check(lh::launch_attn_rowstats(d, BH, (int)S, dout, io == LH_BF16, o, lse,
+                                                 io == LH_BF16 ? wsf : nullptr, io == LH_BF16 ? nullptr : wsf, hs),
+                        "attention row terms")) != LH_OK)
+      return st;
+  }
+  for (int part = 0; part < 2; ++part) {
+    Span sp(part == 0 ? LH_STAGE_ATTN_BWD_DQ : LH_STAGE_ATTN_BWD_DKDV, hs);
+    hipError_t e;
+    if (io == LH_BF16)
+      e = lh::launch_attn_bwd_mfma(d, BH, (int)S, (int)S, q, k, v, dout, wsf, dq, dk, dv, part, hs);
+    else
+      e = lh::launch_attn_bwd_valu(io, d, BH, (int)S, (int)S, q, k, v, o, lse, reinterpret_cast<const float *>(dout),
+                                   wsf, dq, dk, dv, part, hs);
+    if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  }
+  return LH_OK;
 }
 
 const char *lh_stage_name(int stage) {

@@ -55,6 +55,8 @@ _lib.lh_backward.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _sz, _vp, _vp, _vp, _i
 _lib.lh_backward.restype = _i
 _lib.lh_attention_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp]
 _lib.lh_attention_forward.restype = _i
+_lib.lh_attention_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp, _sz, _vp]
+_lib.lh_attention_backward.restype = _i
 _lib.lh_status_string.argtypes = [_i]
 _lib.lh_status_string.restype = ctypes.c_char_p
 _lib.lh_last_error.argtypes = []
@@ -164,6 +166,17 @@ def lh_backward(q, k, v, dout, dout_dtype, saved, saved_bytes, dq, dk, dv, grad_
 def lh_attention_forward(q, k, v, o, lse, BH, S, d, io, stream=None):
     return _lib.lh_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, S, d, dtype_code(io),
                                      _stream(stream))
+
+
+def lh_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, ws, ws_bytes, stream=None):
+    return _lib.lh_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), BH, S, d, dtype_code(io), _ptr(ws), ws_bytes,
+                                      _stream(stream))
+
+
+def attention_backward_ws_bytes(BH, S, io) -> int:
+    """Workspace lh_attention_backward needs (see lighthouse.h)."""
+    return (8 if dtype_code(io) == LH_BF16 else 4) * BH * S
 
 
 # ---------------------------------------------------------------------------

@@ -123,6 +123,20 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
 lh_status lh_attention_forward(const void *q, const void *k, const void *v, float *o, float *lse,
                                int BH, int64_t S, int d, lh_dtype io, void *stream);
 
+/* Backward of lh_attention_forward (Sec. 3.1 Eq. 1; Sec. 3.2): with P
+ * recomputed from the forward's LSE, delta = rowsum(dO o O),
+ *   dV = P^T dO,  dS = P o (dO V^T - delta),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
+ *   q, k, v : [BH][S][d] dtype `io`, as given to lh_attention_forward.
+ *   o, lse  : its outputs, [BH][S][d] and [BH][S] fp32 (lse non-NULL).
+ *   dout    : [BH][S][d] dtype `io`.
+ *   dq, dk, dv : [BH][S][d] fp32 (overwritten).
+ *   ws      : >= 8*BH*S bytes (LH_BF16) or 4*BH*S bytes (LH_F32); contents undefined after.
+ * LH_BF16 needs S to be a multiple of 64 (whole 64-row tiles), else LH_EUNSUPPORTED.
+ * Deterministic (no floating-point atomics). */
+lh_status lh_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                                const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
+                                lh_dtype io, void *ws, size_t ws_bytes, void *stream);
+
 /* Stages of lh_forward / lh_backward, for stage timing. */
 typedef enum {
   LH_STAGE_POOL_SCORE = 0,   /* (i)+(ii): pyramid and scores, one pass over Q, K, V          */

@@ -103,6 +103,17 @@ def test_forward_validation_before_launch(lh):
                           "f32", fake, bws) == 1
     # dense attention: unsupported d
     assert lh.lh_attention_forward(fake, fake, fake, fake, None, 1, 128, 80, "bf16") == 3
+    # dense attention backward: bf16 needs S % 64 == 0, workspace size, null lse, misaligned gradient
+    bw = lh.attention_backward_ws_bytes(2, 128, "bf16")
+    assert bw == 8 * 2 * 128 and lh.attention_backward_ws_bytes(2, 100, "f32") == 4 * 2 * 100
+    args = (fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert lh.lh_attention_backward(*args, 2, 100, 64, "bf16", fake, 8 * 2 * 100) == 3
+    assert lh.lh_attention_backward(*args, 2, 128, 64, "bf16", fake, bw - 1) == 4
+    assert lh.lh_attention_backward(fake, fake, fake, fake, None, fake, fake, fake, fake, 2, 128, 64, "bf16", fake,
+                                    bw) == 1
+    assert lh.lh_attention_backward(fake, fake, fake, fake, fake, fake, fake + 8, fake, fake, 2, 100, 64, "f32",
+                                    fake, 800) == 1
+    assert lh.lh_attention_backward(*args, 2, 128, 96, "bf16", fake, bw) == 3
 
 
 def test_stage_timing_host_side(lh):
