@@ -178,6 +178,19 @@ def test_98k_bf16(lh):
     _run(lh, cfg, full_attention=False, sample_rows=192, e2e=False, heads=[0, 3, 7])
 
 
+@pytest.mark.parametrize("L,p,k", [
+    (3, 2, 1536),   # p = 2: pooling fan-in 2, up to 3 contributors per position
+    (5, 2, 2048),   # five levels
+    (4, 4, 3072),
+    (3, 4, 6144),   # the largest k of the pages' grid
+])
+def test_ablation_grid_98k_bf16(lh, L, p, k):
+    """Shapes of the pages' ablation grid at N = 98,304 (one head): selection,
+    order and scatter exact; attention on sampled rows."""
+    cfg = synth.config("98k", H=1, L=L, p=p, k=k)
+    _run(lh, cfg, full_attention=False, sample_rows=128, e2e=False)
+
+
 def test_deterministic(lh):
     import torch
     cfg = synth.config("bwd8k", N=16384)
