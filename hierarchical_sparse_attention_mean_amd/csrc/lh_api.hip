@@ -219,6 +219,129 @@ void bwd_ws_layout(const lh::Shape &s, lh::BwdWs *w) {
   w->total = cur;
 }
 
+// ---- projection-inclusive layer ----
+
+lh_status make_layer(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk, lh_dtype io,
+                     lh::Shape *s) {
+  lh_status st = make_shape(B, H, N, d, L, p, topk, io, s);
+  if (st != LH_OK) return st;
+  if (d_model < 64 || d_model % 64 != 0 || d_model > (1 << 16))
+    return fail(LH_EUNSUPPORTED, "d_model must be a positive multiple of 64, at most 65536 (got %d)", d_model);
+  if ((int64_t)H * d > (1 << 16)) return fail(LH_EUNSUPPORTED, "H*d must be at most 65536");
+  return LH_OK;
+}
+
+void layer_layout(const lh::Shape &s, int d_model, lh_layer_layout_t *o) {
+  (void)d_model;
+  const size_t head = elem_size(s.io) * (size_t)s.BH * (size_t)s.N * (size_t)s.d;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  o->q = take(head);
+  o->k = take(head);
+  o->v = take(head);
+  o->o = take(head);
+  lh_saved_layout_t inner;
+  saved_layout(s, &inner);
+  o->inner = take(inner.total);
+  o->inner_bytes = inner.total;
+  o->total = cur;
+}
+
+// Weight gradients contract over the N tokens of each batch element: split the
+// contraction so that the product has about 1024 work-groups; partials are
+// [B][splits][M][N] fp32.
+void wgrad_split(int M, int Nc, int64_t N, int io, int *splits, int *kchunk) {
+  const int tm = io == LH_BF16 ? 256 : 64;
+  const int64_t tiles = ((M + tm - 1) / tm) * (int64_t)((Nc + tm - 1) / tm);
+  const int64_t target = tiles >= 1024 ? 1 : 1024 / tiles;
+  int64_t kc = (N + target - 1) / target;
+  kc = (kc + 31) / 32 * 32;
+  if (kc < 256) kc = 256;
+  *kchunk = (int)kc;
+  *splits = (int)((N + kc - 1) / kc);
+}
+
+// Backward workspace of the layer: dO, dQ, dK, dV in the head layout (io dtype),
+// the inner backward workspace, and the fp32 split-K partials of the weight
+// gradients (sized for the larger of X^T [dQ dK dV] and O^T dY).
+struct LayerBwdWs {
+  size_t dout, dq, dk, dv, inner, inner_bytes, part, total;
+  int split_qkv, kchunk_qkv, split_o, kchunk_o;
+};
+
+void layer_bwd_layout(const lh::Shape &s, int B, int H, int d_model, LayerBwdWs *w) {
+  const size_t head = elem_size(s.io) * (size_t)s.BH * (size_t)s.N * (size_t)s.d;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  w->dout = take(head);
+  w->dq = take(head);
+  w->dk = take(head);
+  w->dv = take(head);
+  lh::BwdWs bw;
+  bwd_ws_layout(s, &bw);
+  w->inner = take(bw.total);
+  w->inner_bytes = bw.total;
+  const int Hd = H * s.d;
+  wgrad_split(d_model, 3 * Hd, s.N, s.io, &w->split_qkv, &w->kchunk_qkv);
+  wgrad_split(Hd, d_model, s.N, s.io, &w->split_o, &w->kchunk_o);
+  const size_t pq = (size_t)B * w->split_qkv * (size_t)d_model * 3 * Hd;
+  const size_t po = (size_t)B * w->split_o * (size_t)Hd * d_model;
+  w->part = take(4 * (pq > po ? pq : po));
+  w->total = cur;
+}
+
+// Row-major [R][C] per batch element (bstride elements apart).
+lh::MatView view_plain(const void *p, long long C, long long bstride) {
+  lh::MatView v{};
+  v.p[0] = v.p[1] = v.p[2] = p;
+  v.seg = v.hd = C;
+  v.ld = C;
+  v.bstride = bstride;
+  return v;
+}
+// Head layout [B][H][N][d] of up to three tensors, as the [N][n H d] matrix of
+// the layer (n = number of tensors: columns [i H d, (i+1) H d) are tensor i).
+lh::MatView view_heads(const void *p0, const void *p1, const void *p2, int H, int64_t N, int d) {
+  lh::MatView v{};
+  v.p[0] = p0;
+  v.p[1] = p1;
+  v.p[2] = p2;
+  v.seg = (long long)H * d;
+  v.hd = d;
+  v.hstride = N * d;
+  v.ld = d;
+  v.bstride = (long long)H * N * d;
+  return v;
+}
+// Up to three [R][C] matrices side by side as one [R][n C] matrix.
+lh::MatView view_side(const void *p0, const void *p1, const void *p2, long long C) {
+  lh::MatView v = view_plain(p0, C, 0);
+  v.p[1] = p1;
+  v.p[2] = p2;
+  return v;
+}
+
+lh::GemmArgs gemm(int M, int N, int K, const lh::MatView &a, const lh::MatView &b, const lh::MatView &c) {
+  lh::GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a;
+  g.b = b;
+  g.c = c;
+  g.kchunk = K;
+  g.splits = 1;
+  return g;
+}
+
 lh_status hip_check(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(LH_EHIP, "%s: %s", what, hipGetErrorString(e));
   return LH_OK;
@@ -462,6 +585,144 @@ lh_status lh_attention_backward(const void *q, const void *k, const void *v, con
   return LH_OK;
 }
 
+lh_status lh_layer_query(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk, lh_dtype io,
+                         int64_t *S, size_t *saved_bytes, size_t *fwd_ws_bytes, size_t *bwd_ws_bytes) {
+  lh::Shape s;
+  lh_status st = make_layer(B, H, N, d_model, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  lh_layer_layout_t ll;
+  layer_layout(s, d_model, &ll);
+  lh::FwdWs fw;
+  fwd_ws_layout(s, &fw);
+  LayerBwdWs bw;
+  layer_bwd_layout(s, B, H, d_model, &bw);
+  if (S) *S = s.S;
+  if (saved_bytes) *saved_bytes = ll.total;
+  if (fwd_ws_bytes) *fwd_ws_bytes = fw.total;
+  if (bwd_ws_bytes) *bwd_ws_bytes = bw.total;
+  return LH_OK;
+}
+
+lh_status lh_layer_saved_layout(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk, lh_dtype io,
+                                lh_layer_layout_t *out) {
+  if (!out) return fail(LH_EINVAL, "out is NULL");
+  lh::Shape s;
+  lh_status st = make_layer(B, H, N, d_model, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  layer_layout(s, d_model, out);
+  return LH_OK;
+}
+
+lh_status lh_layer_forward(const void *x, const void *wq, const void *wk, const void *wv, const void *wo, void *y,
+                           lh_dtype y_dtype, int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk,
+                           lh_dtype io, void *saved, size_t saved_bytes, void *ws, size_t ws_bytes, void *stream) {
+  lh::Shape s;
+  lh_status st = make_layer(B, H, N, d_model, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  if (y_dtype != LH_F32 && y_dtype != LH_BF16) return fail(LH_EINVAL, "y_dtype must be LH_F32 or LH_BF16");
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) || !aligned16(wo) || !aligned16(y))
+    return fail(LH_EINVAL, "x, wq, wk, wv, wo, y must be non-NULL and 16-byte aligned");
+  if (!aligned16(saved) || !aligned16(ws)) return fail(LH_EINVAL, "saved and ws must be non-NULL and 16-byte aligned");
+  lh_layer_layout_t ll;
+  layer_layout(s, d_model, &ll);
+  lh::FwdWs fw;
+  fwd_ws_layout(s, &fw);
+  if (saved_bytes < ll.total)
+    return fail(LH_EWORKSPACE, "saved buffer too small: %zu < %zu bytes", saved_bytes, ll.total);
+  if (ws_bytes < fw.total) return fail(LH_EWORKSPACE, "forward workspace too small: %zu < %zu bytes", ws_bytes, fw.total);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  char *sv = reinterpret_cast<char *>(saved);
+  const int Hd = H * d;
+  // Q, K, V = X W_Q, X W_K, X W_V, written in the head layout
+  {
+    Span sp(LH_STAGE_PROJ, hs);
+    const lh::GemmArgs g = gemm((int)N, 3 * Hd, d_model, view_plain(x, d_model, N * d_model),
+                                view_side(wq, wk, wv, Hd), view_heads(sv + ll.q, sv + ll.k, sv + ll.v, H, N, d));
+    if ((st = hip_check(lh::launch_gemm(g, true, false, io, io, B, hs), "projection")) != LH_OK) return st;
+  }
+  // the Lighthouse attention of every head
+  if ((st = lh_forward(sv + ll.q, sv + ll.k, sv + ll.v, sv + ll.o, io, B, H, N, d, L, p, topk, io, sv + ll.inner,
+                       ll.inner_bytes, ws, ws_bytes, stream)) != LH_OK)
+    return st;
+  // Y = [O_0 .. O_{H-1}] W_O
+  {
+    Span sp(LH_STAGE_OUT_PROJ, hs);
+    const lh::GemmArgs g = gemm((int)N, d_model, Hd, view_heads(sv + ll.o, nullptr, nullptr, H, N, d),
+                                view_plain(wo, d_model, 0), view_plain(y, d_model, N * d_model));
+    if ((st = hip_check(lh::launch_gemm(g, true, false, io, y_dtype, B, hs), "output projection")) != LH_OK)
+      return st;
+  }
+  return LH_OK;
+}
+
+lh_status lh_layer_backward(const void *x, const void *wq, const void *wk, const void *wv, const void *wo,
+                            const void *dy, const void *saved, size_t saved_bytes, void *dx, lh_dtype dx_dtype,
+                            float *dwq, float *dwk, float *dwv, float *dwo, int B, int H, int64_t N, int d_model,
+                            int d, int L, int p, int64_t topk, lh_dtype io, void *ws, size_t ws_bytes, void *stream) {
+  lh::Shape s;
+  lh_status st = make_layer(B, H, N, d_model, d, L, p, topk, io, &s);
+  if (st != LH_OK) return st;
+  if (dx_dtype != LH_F32 && dx_dtype != LH_BF16) return fail(LH_EINVAL, "dx_dtype must be LH_F32 or LH_BF16");
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) || !aligned16(wo) || !aligned16(dy))
+    return fail(LH_EINVAL, "x, wq, wk, wv, wo, dy must be non-NULL and 16-byte aligned");
+  if (!aligned16(dx) || !aligned16(dwq) || !aligned16(dwk) || !aligned16(dwv) || !aligned16(dwo))
+    return fail(LH_EINVAL, "dx, dwq, dwk, dwv, dwo must be non-NULL and 16-byte aligned");
+  if (!aligned16(saved) || !aligned16(ws)) return fail(LH_EINVAL, "saved and ws must be non-NULL and 16-byte aligned");
+  lh_layer_layout_t ll;
+  layer_layout(s, d_model, &ll);
+  LayerBwdWs bw;
+  layer_bwd_layout(s, B, H, d_model, &bw);
+  if (saved_bytes < ll.total)
+    return fail(LH_EWORKSPACE, "saved buffer too small: %zu < %zu bytes", saved_bytes, ll.total);
+  if (ws_bytes < bw.total) return fail(LH_EWORKSPACE, "backward workspace too small: %zu < %zu bytes", ws_bytes, bw.total);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const char *sv = reinterpret_cast<const char *>(saved);
+  char *wb = reinterpret_cast<char *>(ws);
+  float *part = reinterpret_cast<float *>(wb + bw.part);
+  const int Hd = H * d;
+  const lh::MatView vdy = view_plain(dy, d_model, N * d_model);
+  // dO = dY W_O^T (head layout) and dW_O = O^T dY
+  {
+    Span sp(LH_STAGE_OUT_PROJ_BWD, hs);
+    const lh::GemmArgs g = gemm((int)N, Hd, d_model, vdy, view_plain(wo, d_model, 0),
+                                view_heads(wb + bw.dout, nullptr, nullptr, H, N, d));
+    if ((st = hip_check(lh::launch_gemm(g, true, true, io, io, B, hs), "dO")) != LH_OK) return st;
+    lh::GemmArgs gw = gemm(Hd, d_model, (int)N, view_heads(sv + ll.o, nullptr, nullptr, H, N, d), vdy,
+                           view_plain(part, d_model, (long long)bw.split_o * Hd * d_model));
+    gw.kchunk = bw.kchunk_o;
+    gw.splits = bw.split_o;
+    gw.zstride = (long long)Hd * d_model;
+    if ((st = hip_check(lh::launch_gemm(gw, false, false, io, LH_F32, B, hs), "dW_O")) != LH_OK) return st;
+    if ((st = hip_check(lh::launch_split_reduce(part, B * bw.split_o, Hd, d_model, view_plain(dwo, d_model, 0), hs),
+                        "dW_O reduce")) != LH_OK)
+      return st;
+  }
+  // dQ, dK, dV through the Lighthouse attention (selection frozen)
+  if ((st = lh_backward(sv + ll.q, sv + ll.k, sv + ll.v, wb + bw.dout, io, sv + ll.inner, ll.inner_bytes, wb + bw.dq,
+                        wb + bw.dk, wb + bw.dv, io, B, H, N, d, L, p, topk, io, wb + bw.inner, bw.inner_bytes,
+                        stream)) != LH_OK)
+    return st;
+  // dX = dQ W_Q^T + dK W_K^T + dV W_V^T and dW_{Q,K,V} = X^T d{Q,K,V}
+  {
+    Span sp(LH_STAGE_PROJ_BWD, hs);
+    const lh::MatView vg = view_heads(wb + bw.dq, wb + bw.dk, wb + bw.dv, H, N, d);
+    const lh::GemmArgs g = gemm((int)N, d_model, 3 * Hd, vg, view_side(wq, wk, wv, Hd),
+                                view_plain(dx, d_model, N * d_model));
+    if ((st = hip_check(lh::launch_gemm(g, true, true, io, dx_dtype, B, hs), "dX")) != LH_OK) return st;
+    lh::GemmArgs gw = gemm(d_model, 3 * Hd, (int)N, view_plain(x, d_model, N * d_model), vg,
+                           view_plain(part, 3 * Hd, (long long)bw.split_qkv * d_model * 3 * Hd));
+    gw.kchunk = bw.kchunk_qkv;
+    gw.splits = bw.split_qkv;
+    gw.zstride = (long long)d_model * 3 * Hd;
+    if ((st = hip_check(lh::launch_gemm(gw, false, false, io, LH_F32, B, hs), "dW_QKV")) != LH_OK) return st;
+    if ((st = hip_check(lh::launch_split_reduce(part, B * bw.split_qkv, d_model, 3 * Hd, view_side(dwq, dwk, dwv, Hd),
+                                                hs),
+                        "dW_QKV reduce")) != LH_OK)
+      return st;
+  }
+  return LH_OK;
+}
+
 const char *lh_stage_name(int stage) {
   switch (stage) {
     case LH_STAGE_POOL_SCORE: return "pool_score";
@@ -473,6 +734,10 @@ const char *lh_stage_name(int stage) {
     case LH_STAGE_ATTN_BWD_DQ: return "attn_bwd_dq";
     case LH_STAGE_ATTN_BWD_DKDV: return "attn_bwd_dkdv";
     case LH_STAGE_POOL_BWD: return "pool_bwd";
+    case LH_STAGE_PROJ: return "proj";
+    case LH_STAGE_OUT_PROJ: return "out_proj";
+    case LH_STAGE_OUT_PROJ_BWD: return "out_proj_bwd";
+    case LH_STAGE_PROJ_BWD: return "proj_bwd";
     default: return "unknown";
   }
 }

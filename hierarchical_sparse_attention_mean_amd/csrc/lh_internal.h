@@ -69,6 +69,28 @@ struct BwdWs {
   size_t total;
 };
 
+// Matrix view for the layer's products: element (r, c) of a matrix whose column
+// index c runs over up to three stored matrices side by side (which = c / seg),
+// each made of column blocks of width hd stored hstride elements apart:
+//   elem(b, r, c) = p[which] + b bstride + (cc / hd) hstride + r ld + cc % hd,   cc = c % seg.
+// Row-major [R][C]: seg = hd = C, hstride = 0, ld = C.  Head layout [B][H][N][d]
+// seen as the [N][H d] matrix of a layer: seg = H d, hd = d, hstride = N d, ld = d,
+// bstride = H N d.  Element offsets, not bytes.
+struct MatView {
+  const void *p[3];
+  long long seg, hd, hstride, ld, bstride;
+};
+
+// C[m][n] = sum_k A[m][k] B[k][n] for m < M, n < N, k < K, per batch element.
+// Split-K: split z covers k in [z kchunk, min(K, (z+1) kchunk)) and writes its
+// partial product at C + z zstride (elements).
+struct GemmArgs {
+  int M, N, K;
+  MatView a, b, c;
+  int kchunk, splits;
+  long long zstride;
+};
+
 // ---- bf16 helpers (storage is raw uint16 bit patterns) ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((unsigned int)b) << 16);
@@ -105,5 +127,11 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
                               hipStream_t st);
 hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, const float *dkt,
                            const float *dvt, void *dq, void *dk, void *dv, int grad_dtype, hipStream_t st);
+// akm / bkm: A / B k-major (view (r, c) = (m, k) / (n, k)), else mn-major ((k, m) / (k, n)).
+// io: operand dtype (LH_BF16: MFMA; LH_F32: vector ALU).  grid.y = batch.
+int gemm_blocks(const GemmArgs &g, int io);
+hipError_t launch_gemm(const GemmArgs &g, bool akm, bool bkm, int io, int out_dtype, int batch, hipStream_t st);
+// out(r, c) (fp32) = sum over the nparts fp32 partials [nparts][M][N], in order.
+hipError_t launch_split_reduce(const float *part, int nparts, int M, int N, const MatView &out, hipStream_t st);
 
 }  // namespace lh

@@ -42,6 +42,10 @@ class SavedLayout(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("P", "E", "Bsel", "S", "Sv")]
 
 
+class LayerLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "v", "o", "inner", "inner_bytes", "total")]
+
+
 _i, _i64, _sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 _P = ctypes.POINTER
 _lib.lh_query.argtypes = [_i, _i, _i64, _i, _i, _i, _i64, _i, _P(_i64), _P(_sz), _P(_sz), _P(_sz)]
@@ -57,6 +61,16 @@ _lib.lh_attention_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i,
 _lib.lh_attention_forward.restype = _i
 _lib.lh_attention_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp, _sz, _vp]
 _lib.lh_attention_backward.restype = _i
+_lib.lh_layer_query.argtypes = [_i, _i, _i64, _i, _i, _i, _i, _i64, _i, _P(_i64), _P(_sz), _P(_sz), _P(_sz)]
+_lib.lh_layer_query.restype = _i
+_lib.lh_layer_saved_layout.argtypes = [_i, _i, _i64, _i, _i, _i, _i, _i64, _i, _P(LayerLayout)]
+_lib.lh_layer_saved_layout.restype = _i
+_lib.lh_layer_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i64, _i, _i, _i, _i, _i64, _i,
+                                  _vp, _sz, _vp, _sz, _vp]
+_lib.lh_layer_forward.restype = _i
+_lib.lh_layer_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i, _vp, _vp, _vp, _vp,
+                                   _i, _i, _i64, _i, _i, _i, _i, _i64, _i, _vp, _sz, _vp]
+_lib.lh_layer_backward.restype = _i
 _lib.lh_status_string.argtypes = [_i]
 _lib.lh_status_string.restype = ctypes.c_char_p
 _lib.lh_last_error.argtypes = []
@@ -67,7 +81,7 @@ _lib.lh_timing_begin.argtypes = []
 _lib.lh_timing_begin.restype = _i
 _lib.lh_timing_end.argtypes = [_P(ctypes.c_double), _P(_i), _i]
 _lib.lh_timing_end.restype = _i
-STAGE_COUNT = 9   # LH_STAGE_COUNT
+STAGE_COUNT = 13   # LH_STAGE_COUNT
 
 
 def library():
@@ -174,6 +188,36 @@ def lh_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, ws, w
                                       _stream(stream))
 
 
+def lh_layer_query(B, H, N, d_model, d, L, p, topk, io):
+    """Returns (status, S, saved_bytes, fwd_ws_bytes, bwd_ws_bytes)."""
+    S, a, b, c = _i64(), _sz(), _sz(), _sz()
+    st = _lib.lh_layer_query(B, H, N, d_model, d, L, p, topk, dtype_code(io), ctypes.byref(S), ctypes.byref(a),
+                             ctypes.byref(b), ctypes.byref(c))
+    return st, S.value, a.value, b.value, c.value
+
+
+def lh_layer_saved_layout(B, H, N, d_model, d, L, p, topk, io):
+    """Returns (status, dict of byte offsets and sizes)."""
+    out = LayerLayout()
+    st = _lib.lh_layer_saved_layout(B, H, N, d_model, d, L, p, topk, dtype_code(io), ctypes.byref(out))
+    return st, {n: getattr(out, n) for n, _ in LayerLayout._fields_}
+
+
+def lh_layer_forward(x, wq, wk, wv, wo, y, y_dtype, B, H, N, d_model, d, L, p, topk, io, saved, saved_bytes, ws,
+                     ws_bytes, stream=None):
+    return _lib.lh_layer_forward(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(y), dtype_code(y_dtype), B, H,
+                                 N, d_model, d, L, p, topk, dtype_code(io), _ptr(saved), saved_bytes, _ptr(ws),
+                                 ws_bytes, _stream(stream))
+
+
+def lh_layer_backward(x, wq, wk, wv, wo, dy, saved, saved_bytes, dx, dx_dtype, dwq, dwk, dwv, dwo, B, H, N, d_model,
+                      d, L, p, topk, io, ws, ws_bytes, stream=None):
+    return _lib.lh_layer_backward(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(dy), _ptr(saved),
+                                  saved_bytes, _ptr(dx), dtype_code(dx_dtype), _ptr(dwq), _ptr(dwk), _ptr(dwv),
+                                  _ptr(dwo), B, H, N, d_model, d, L, p, topk, dtype_code(io), _ptr(ws), ws_bytes,
+                                  _stream(stream))
+
+
 def attention_backward_ws_bytes(BH, S, io) -> int:
     """Workspace lh_attention_backward needs (see lighthouse.h)."""
     return (8 if dtype_code(io) == LH_BF16 else 4) * BH * S
@@ -277,3 +321,63 @@ class LighthouseAttention(torch.autograd.Function):
         q, k, v, saved = ctx.saved_tensors
         dq, dk, dv = backward(q, k, v, do, saved, ctx.plan)
         return dq, dk, dv, None, None, None
+
+
+# ---------------------------------------------------------------------------
+# projection-inclusive layer
+# ---------------------------------------------------------------------------
+class LayerPlan:
+    """Sizes and layouts for one (B, H, N, d_model, d, L, p, topk, io) layer."""
+
+    def __init__(self, B, H, N, d_model, d, L, p, topk, io):
+        self.B, self.H, self.N, self.d_model, self.d = B, H, N, d_model, d
+        self.L, self.p, self.topk, self.io = L, p, topk, dtype_code(io)
+        st, self.S, self.saved_bytes, self.fwd_ws_bytes, self.bwd_ws_bytes = lh_layer_query(*self.args())
+        _check(st, "lh_layer_query")
+        st, self.layout = lh_layer_saved_layout(*self.args())
+        _check(st, "lh_layer_saved_layout")
+        self.inner = Plan(B, H, N, d, L, p, topk, self.io)
+
+    def args(self):
+        return (self.B, self.H, self.N, self.d_model, self.d, self.L, self.p, self.topk, self.io)
+
+    def view(self, saved, name):
+        """q, k, v, o [B, H, N, d] (io dtype) inside the layer's saved buffer, or
+        the Lighthouse saved buffer itself ('inner')."""
+        if name == "inner":
+            off = self.layout["inner"]
+            return saved[off:off + self.layout["inner_bytes"]]
+        io = torch.bfloat16 if self.io == LH_BF16 else torch.float32
+        n = self.B * self.H * self.N * self.d
+        off = self.layout[name]
+        return saved[off:off + n * (2 if self.io == LH_BF16 else 4)].view(io).view(self.B, self.H, self.N, self.d)
+
+
+def layer_forward(x, wq, wk, wv, wo, H, L, p, topk, y_dtype=None, plan=None, saved=None, ws=None):
+    """Y of the layer for x [B, N, d_model].  Returns (y, saved, plan)."""
+    B, N, dm = x.shape
+    d = wq.shape[1] // H
+    plan = plan or LayerPlan(B, H, N, dm, d, L, p, topk, x.dtype)
+    y_dtype = y_dtype or x.dtype
+    y = torch.empty((B, N, dm), dtype=y_dtype, device=x.device)
+    if saved is None:
+        saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = torch.empty(plan.fwd_ws_bytes, dtype=torch.uint8, device=x.device)
+    st = lh_layer_forward(x, wq, wk, wv, wo, y, y_dtype, *plan.args(), saved, saved.numel(), ws, ws.numel())
+    _check(st, "lh_layer_forward")
+    return y, saved, plan
+
+
+def layer_backward(x, wq, wk, wv, wo, dy, saved, plan, dx_dtype=None, ws=None):
+    """(dx, dwq, dwk, dwv, dwo) with the forward's selection frozen."""
+    dx_dtype = dx_dtype or x.dtype
+    dev = x.device
+    dx = torch.empty(x.shape, dtype=dx_dtype, device=dev)
+    dws = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (wq, wk, wv, wo)]
+    if ws is None:
+        ws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+    st = lh_layer_backward(x, wq, wk, wv, wo, dy.contiguous(), saved, saved.numel(), dx, dx_dtype, *dws,
+                           *plan.args(), ws, ws.numel())
+    _check(st, "lh_layer_backward")
+    return (dx, *dws)

@@ -18,17 +18,27 @@ Random streams: tensor s (0=Q, 1=K, 2=V, 4=dO) of head j (= b*H + h) uses
 SeedSequence(seed, spawn_key=(s, j)); the row positions / multipliers, shared by
 all heads, use spawn_key=(3,).  Any single head can therefore be regenerated on
 its own.
+
+Projection-inclusive layer (``layer_inputs``): d_model = 1024 for the bf16
+workloads (the pages' 530M decoder: d_model 1024, 8 heads of 128), 128 for tiny.
+X [B, N, d_model] and dY are iid N(0,1), X rows scaled by the same per-row
+multipliers as Q and K above; W_Q, W_K, W_V [d_model, H d] are iid
+N(0, 1/d_model) and W_O [H d, d_model] iid N(0, 1/(H d)), so that the
+projections have unit variance.  Streams: spawn_key=(10 + i, b) for X (i=0) and
+dY (i=1) of batch element b, spawn_key=(20 + i,) for W_Q, W_K, W_V, W_O.
 """
 from __future__ import annotations
 
 import numpy as np
 
 CONFIGS = {
-    "tiny":  dict(index=0, B=1, H=2, d=64, N=1024, L=3, p=4, k=64, dtype="f32", recipe="mod97x4"),
-    "98k":   dict(index=1, B=1, H=8, d=128, N=98304, L=3, p=4, k=768, dtype="bf16", recipe="pct1x3"),
-    "512k":  dict(index=2, B=1, H=8, d=128, N=524288, L=3, p=4, k=4096, dtype="bf16", recipe="pct1x3"),
-    "1m":    dict(index=3, B=1, H=8, d=128, N=1048576, L=4, p=4, k=4096, dtype="bf16", recipe="zipf"),
-    "bwd8k": dict(index=4, B=1, H=8, d=128, N=8192, L=3, p=4, k=64, dtype="bf16", recipe="pct1x3"),
+    "tiny":  dict(index=0, B=1, H=2, d=64, N=1024, L=3, p=4, k=64, dtype="f32", recipe="mod97x4", d_model=128),
+    "98k":   dict(index=1, B=1, H=8, d=128, N=98304, L=3, p=4, k=768, dtype="bf16", recipe="pct1x3", d_model=1024),
+    "512k":  dict(index=2, B=1, H=8, d=128, N=524288, L=3, p=4, k=4096, dtype="bf16", recipe="pct1x3",
+                  d_model=1024),
+    "1m":    dict(index=3, B=1, H=8, d=128, N=1048576, L=4, p=4, k=4096, dtype="bf16", recipe="zipf",
+                  d_model=1024),
+    "bwd8k": dict(index=4, B=1, H=8, d=128, N=8192, L=3, p=4, k=64, dtype="bf16", recipe="pct1x3", d_model=1024),
 }
 
 SEED_BASE = 20260
@@ -115,3 +125,27 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def layer_inputs(cfg: dict, with_dy: bool = False) -> dict:
+    """x [B, N, d_model], wq, wk, wv [d_model, H d], wo [H d, d_model] (and dy
+    [B, N, d_model]) in storage format (see the module notes)."""
+    B, N, H, d, dm = cfg["B"], cfg["N"], cfg["H"], cfg["d"], cfg["d_model"]
+    mult = row_multipliers(cfg)
+    conv = f32_to_bf16_bits if cfg["dtype"] == "bf16" else (lambda a: a)
+    out = {}
+    xs = []
+    for b in range(B):
+        x = _rng(cfg["seed"], 10, b).standard_normal((N, dm), dtype=np.float32)
+        x *= mult[:, None]
+        xs.append(conv(x))
+    out["x"] = np.stack(xs)
+    for i, nm in enumerate(("wq", "wk", "wv")):
+        w = _rng(cfg["seed"], 20 + i).standard_normal((dm, H * d), dtype=np.float32) / np.float32(np.sqrt(dm))
+        out[nm] = conv(w)
+    wo = _rng(cfg["seed"], 23).standard_normal((H * d, dm), dtype=np.float32) / np.float32(np.sqrt(H * d))
+    out["wo"] = conv(wo)
+    if with_dy:
+        out["dy"] = np.stack([conv(_rng(cfg["seed"], 11, b).standard_normal((N, dm), dtype=np.float32))
+                              for b in range(B)])
+    return out

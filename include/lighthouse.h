@@ -137,7 +137,58 @@ lh_status lh_attention_backward(const void *q, const void *k, const void *v, con
                                 const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
                                 lh_dtype io, void *ws, size_t ws_bytes, void *stream);
 
-/* Stages of lh_forward / lh_backward, for stage timing. */
+/* ---- Projection-inclusive layer ----
+ * The attention layer of the decoder the pages train, around the Lighthouse
+ * attention (Sec. 3.1: Q, K, V in R^{N x d} are the per-head projections
+ * X W_Q, X W_K, X W_V of the layer input X in R^{N x d_model}; Sec. 3.2: the
+ * gradient reaches W_Q, W_K, W_V through the scatter, the sub-sequence attention
+ * and the gather; the selection stays frozen).  The output projection W_O is that
+ * of the Llama-3-style attention block (experiments: d_model = 1024, 8 heads,
+ * head dimension 128):
+ *   Q_h = X W_Q[:, h d:(h+1) d]  (likewise K_h, V_h),   O_h = Lighthouse(Q_h, K_h, V_h),
+ *   Y = [O_0 | ... | O_{H-1}] W_O.
+ * Layouts: x, y, dy, dx [B][N][d_model]; wq, wk, wv [d_model][H d] (head h =
+ * columns h d .. h d + d - 1); wo [H d][d_model]; all row-major.  x, the weights
+ * and dy are in the io dtype.  The products run on bf16 MFMA with fp32
+ * accumulation (LH_BF16) or in fp32 on the vector ALUs (LH_F32).  d_model must be
+ * a multiple of 64.  Conventions as above (caller-owned buffers, validation
+ * first, only enqueues on `stream`).  The backward's weight gradients sum over
+ * every token of the batch with a fixed split and a fixed summation order:
+ * deterministic. */
+typedef struct lh_layer_layout_t {
+  size_t q, k, v;     /* io [B][H][N][d] projected Q, K, V (the Lighthouse inputs)        */
+  size_t o;           /* io [B][H][N][d] Lighthouse output O (the input of W_O)           */
+  size_t inner;       /* the lh_forward `saved` buffer of the attention (lh_saved_layout) */
+  size_t inner_bytes; /* its size                                                         */
+  size_t total;       /* bytes needed                                                     */
+} lh_layer_layout_t;
+
+/* Host-only.  Validates the layer shape; returns S and the byte sizes of the
+ * layer's `saved` buffer and of its forward and backward workspaces. */
+lh_status lh_layer_query(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk, lh_dtype io,
+                         int64_t *S, size_t *saved_bytes, size_t *fwd_ws_bytes, size_t *bwd_ws_bytes);
+
+/* Host-only.  Offsets inside the layer's `saved` buffer. */
+lh_status lh_layer_saved_layout(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk,
+                                lh_dtype io, lh_layer_layout_t *out);
+
+/* Forward of the layer: projections, Lighthouse attention of every head, output
+ * projection.  y in dtype y_dtype (LH_F32 or LH_BF16).  saved: >= saved_bytes of
+ * lh_layer_query, filled for lh_layer_backward.  ws: >= fwd_ws_bytes. */
+lh_status lh_layer_forward(const void *x, const void *wq, const void *wk, const void *wv, const void *wo, void *y,
+                           lh_dtype y_dtype, int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk,
+                           lh_dtype io, void *saved, size_t saved_bytes, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of the layer for upstream gradient dy (io dtype): dx in dx_dtype
+ * (LH_F32 or LH_BF16); dwq, dwk, dwv [d_model][H d] and dwo [H d][d_model] in
+ * fp32 (overwritten).  saved: the buffer lh_layer_forward filled for the same
+ * x and weights.  ws: >= bwd_ws_bytes of lh_layer_query. */
+lh_status lh_layer_backward(const void *x, const void *wq, const void *wk, const void *wv, const void *wo,
+                            const void *dy, const void *saved, size_t saved_bytes, void *dx, lh_dtype dx_dtype,
+                            float *dwq, float *dwk, float *dwv, float *dwo, int B, int H, int64_t N, int d_model,
+                            int d, int L, int p, int64_t topk, lh_dtype io, void *ws, size_t ws_bytes, void *stream);
+
+/* Stages of lh_forward / lh_backward (and of the layer entry points), for stage timing. */
 typedef enum {
   LH_STAGE_POOL_SCORE = 0,   /* (i)+(ii): pyramid and scores, one pass over Q, K, V          */
   LH_STAGE_TOPK = 1,         /* (ii): joint top-B selection (state clear + 3 passes)          */
@@ -148,7 +199,11 @@ typedef enum {
   LH_STAGE_ATTN_BWD_DQ = 6,  /* adjoint of Eq. 9: dQ~                                         */
   LH_STAGE_ATTN_BWD_DKDV = 7,/* adjoint of Eq. 9: dK~, dV~                                    */
   LH_STAGE_POOL_BWD = 8,     /* adjoint of the gather and of the pooling: dQ, dK, dV          */
-  LH_STAGE_COUNT = 9
+  LH_STAGE_PROJ = 9,         /* layer: Q, K, V = X W_Q, X W_K, X W_V                           */
+  LH_STAGE_OUT_PROJ = 10,    /* layer: Y = O W_O                                               */
+  LH_STAGE_OUT_PROJ_BWD = 11,/* layer: dO = dY W_O^T and dW_O = O^T dY                         */
+  LH_STAGE_PROJ_BWD = 12,    /* layer: dX = dQ W_Q^T + dK W_K^T + dV W_V^T and dW_Q, dW_K, dW_V */
+  LH_STAGE_COUNT = 13
 } lh_stage;
 
 /* Host-only.  Short name of a stage ("attn_bwd_dkdv", ...; static storage). */
@@ -156,7 +211,8 @@ const char *lh_stage_name(int stage);
 
 /* Host-only.  Stage timing, for benchmarks (not part of the compute path).
  * lh_timing_begin switches timing on for the calling host thread and drops
- * any earlier records.  While it is on, lh_forward and lh_backward bracket the
+ * any earlier records.  While it is on, lh_forward, lh_backward and the layer
+ * entry points bracket the
  * kernel launches of each stage with a pair of HIP events recorded on the
  * call's stream -- the only time the library creates anything.
  * lh_timing_end switches it off, waits for the recorded events, and writes for

@@ -13,7 +13,9 @@ BIG = 1 << 40
 def test_exports_every_declared_symbol(lh):
     names = lh.declared_symbols()
     assert set(names) >= {"lh_query", "lh_forward", "lh_backward", "lh_attention_forward", "lh_saved_layout",
-                          "lh_status_string", "lh_last_error"}
+                          "lh_status_string", "lh_last_error", "lh_attention_backward", "lh_layer_query",
+                          "lh_layer_saved_layout", "lh_layer_forward", "lh_layer_backward", "lh_stage_name",
+                          "lh_timing_begin", "lh_timing_end"}
     lib = lh.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -123,7 +125,7 @@ def test_stage_timing_host_side(lh):
     hdr = open(lh.HEADER).read()
     names = [lh.lh_stage_name(i) for i in range(lh.STAGE_COUNT)]
     assert names == ["pool_score", "topk", "gather", "attn_fwd", "scatter", "scatter_bwd", "attn_bwd_dq",
-                     "attn_bwd_dkdv", "pool_bwd"]
+                     "attn_bwd_dkdv", "pool_bwd", "proj", "out_proj", "out_proj_bwd", "proj_bwd"]
     assert lh.lh_stage_name(lh.STAGE_COUNT) == "unknown"
     assert int(re.search(r"LH_STAGE_COUNT\s*=\s*(\d+)", hdr).group(1)) == lh.STAGE_COUNT
     assert lh.lh_timing_begin() == 0
@@ -131,3 +133,55 @@ def test_stage_timing_host_side(lh):
     assert st == 0 and all(ms == 0.0 and s == 0 for ms, s in stages.values())
     assert lh.library().lh_timing_end(None, None, 3) == 1
     assert lh.library().lh_timing_end(None, None, 0) == 0
+
+
+@pytest.mark.parametrize("B,H,N,dm,d,io", [(1, 8, 524288, 1024, 128, "bf16"), (2, 3, 1040, 192, 64, "f32"),
+                                           (1, 2, 1024, 128, 64, "f32"), (2, 3, 1040, 192, 64, "bf16")])
+def test_layer_query_and_layout(lh, B, H, N, dm, d, io):
+    """The layer's saved buffer holds Q, K, V, O in the head layout and then the
+    attention's own saved buffer; the workspaces cover the attention's."""
+    L, p, k = 3, 4, 32
+    st, S, saved, fws, bws = lh.lh_layer_query(B, H, N, dm, d, L, p, k, io)
+    assert st == 0, lh.lh_last_error()
+    st2, S2, isaved, ifws, ibws = lh.lh_query(B, H, N, d, L, p, k, io)
+    assert st2 == 0 and S == S2
+    st, lay = lh.lh_layer_saved_layout(B, H, N, dm, d, L, p, k, io)
+    assert st == 0
+    head = (2 if io == "bf16" else 4) * B * H * N * d
+    order = ["q", "k", "v", "o", "inner"]
+    for a, b in zip(order, order[1:]):
+        assert lay[a] % 256 == 0 and lay[b] - lay[a] >= head
+    assert lay["inner_bytes"] == isaved and lay["inner"] + isaved <= lay["total"] == saved
+    assert fws == ifws
+    assert bws >= 4 * head + ibws
+
+
+def test_layer_validation_before_launch(lh):
+    """Bad layer arguments fail on the host; nothing is enqueued."""
+    B, H, N, dm, d, L, p, k = 1, 2, 1024, 128, 64, 3, 4, 64
+    st, S, saved, fws, bws = lh.lh_layer_query(B, H, N, dm, d, L, p, k, "f32")
+    assert st == 0
+    fake = 1 << 20
+    assert lh.lh_layer_query(B, H, N, 96, d, L, p, k, "f32")[0] == 3        # d_model not a multiple of 64
+    assert lh.lh_layer_query(B, H, N, dm, 96, L, p, k, "f32")[0] == 3       # d unsupported
+    assert lh.lh_layer_query(B, H, 1000, dm, d, L, p, k, "f32")[0] == 2     # p^(L-1) does not divide N
+    ws6 = (fake,) * 6
+    assert lh.lh_layer_forward(*ws6, "f32", B, H, N, dm, d, L, p, k, "f32", fake, saved - 1, fake, fws) == 4
+    assert lh.lh_layer_forward(*ws6, "f32", B, H, N, dm, d, L, p, k, "f32", fake, saved, fake, fws - 1) == 4
+    assert lh.lh_layer_forward(None, *ws6[1:], "f32", B, H, N, dm, d, L, p, k, "f32", fake, saved, fake, fws) == 1
+    assert lh.lh_layer_forward(*ws6[:5], fake + 8, "f32", B, H, N, dm, d, L, p, k, "f32", fake, saved, fake,
+                               fws) == 1
+    assert lh.library().lh_layer_forward(*ws6, 7, B, H, N, dm, d, L, p, k, 0, fake, saved, fake, fws, None) == 1
+    # backward: every call below fails validation (workspace, saved size, null or misaligned gradient, dtype)
+    head = (fake,) * 6                                           # x, wq, wk, wv, wo, dy
+    grads = (fake, fake, fake, fake)                             # dwq, dwk, dwv, dwo
+    assert lh.lh_layer_backward(*head, fake, saved, fake, "f32", *grads, B, H, N, dm, d, L, p, k, "f32", fake,
+                                bws - 1) == 4
+    assert lh.lh_layer_backward(*head, fake, saved - 1, fake, "f32", *grads, B, H, N, dm, d, L, p, k, "f32", fake,
+                                bws) == 4
+    assert lh.lh_layer_backward(*head, fake, saved, fake, "f32", None, fake, fake, fake, B, H, N, dm, d, L, p, k,
+                                "f32", fake, bws) == 1
+    assert lh.lh_layer_backward(*head, fake, saved, fake + 4, "f32", *grads, B, H, N, dm, d, L, p, k, "f32", fake,
+                                bws) == 1
+    assert lh.library().lh_layer_backward(*head, fake, saved, fake, 9, *grads, B, H, N, dm, d, L, p, k, 0, fake, bws,
+                                          None) == 1
