@@ -6,7 +6,7 @@ backward, gather+pool adjoint) for one batch of seeded synthetic bf16 inputs
 already resident in HBM.  Default workload: B=1, H=8, d=128, N=524,288, L=3,
 p=4, k=4,096 (S=65,536).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--dense]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--dense] [--layer]
 
 Prints one JSON line (rank 0).  Besides the contract fields it carries:
   roofline      the dominant kernel of the step (by time): its algorithmic FLOPs
@@ -17,8 +17,11 @@ Prints one JSON line (rank 0).  Besides the contract fields it carries:
                 when the kernel's sources changed since the counters were taken
   cpu_baseline  the fp64 oracle on one head of the same workload (fwd + bwd),
                 on this host's cores, scaled to the layer's tokens/s
-  extra         per-stage times, forward-only time, and (with --dense) the dense
-                causal attention kernel at S = N
+  extra         per-stage times, forward-only time, (with --dense) the dense
+                causal attention kernel at S = N, and (with --layer) the
+                projection-inclusive layer (X -> W_Q, W_K, W_V -> Lighthouse ->
+                W_O, forward and backward) at d_model = 1024 with the TFLOP/s of
+                its four product stages
 """
 from __future__ import annotations
 
@@ -108,6 +111,77 @@ def cpu_baseline(cfg: dict) -> dict:
             "ms_per_step": layer_s * 1e3}
 
 
+def layer_flops(N: int, dm: int, Hd: int) -> dict:
+    """Algorithmic FLOPs of the layer's product stages (2 per multiply-add):
+    proj [Q K V] = X W (N x d_model x 3 H d); out_proj Y = O W_O (N x H d x
+    d_model); out_proj_bwd dO = dY W_O^T and dW_O = O^T dY; proj_bwd dX =
+    [dQ dK dV] W^T and dW = X^T [dQ dK dV]."""
+    return {"proj": 2.0 * N * dm * 3 * Hd, "out_proj": 2.0 * N * Hd * dm,
+            "out_proj_bwd": 2 * 2.0 * N * Hd * dm, "proj_bwd": 2 * 2.0 * N * dm * 3 * Hd}
+
+
+def time_layer(lh, synth, cfg: dict, args, dev) -> dict:
+    """Forward + backward of the projection-inclusive layer on the same workload
+    (bf16 x, weights, y, dy, dx; fp32 weight gradients)."""
+    import numpy as np
+    import torch
+    B, H, N, d, dm = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["d_model"]
+    t0 = time.perf_counter()
+    inp = synth.layer_inputs(cfg, with_dy=True)
+    bf = cfg["dtype"] == "bf16"
+    io = torch.bfloat16 if bf else torch.float32
+    t = {n: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf else torch.from_numpy(a)).to(dev)
+         for n, a in inp.items()}
+    del inp
+    log(f"[bench] layer inputs resident in HBM (d_model={dm}, {time.perf_counter() - t0:.1f} s)")
+    plan = lh.LayerPlan(B, H, N, dm, d, cfg["L"], cfg["p"], cfg["k"], io)
+    y = torch.empty((B, N, dm), dtype=io, device=dev)
+    dx = torch.empty((B, N, dm), dtype=io, device=dev)
+    dws = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (t["wq"], t["wk"], t["wv"], t["wo"])]
+    saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=dev)
+    fws = torch.empty(plan.fwd_ws_bytes, dtype=torch.uint8, device=dev)
+    bws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+    w = (t["x"], t["wq"], t["wk"], t["wv"], t["wo"])
+
+    def fwd():
+        st = lh.lh_layer_forward(*w, y, io, *plan.args(), saved, saved.numel(), fws, fws.numel())
+        if st:
+            raise lh.LighthouseError(st, "lh_layer_forward")
+
+    def bwd():
+        st = lh.lh_layer_backward(*w, t["dy"], saved, saved.numel(), dx, io, *dws, *plan.args(), bws, bws.numel())
+        if st:
+            raise lh.LighthouseError(st, "lh_layer_backward")
+
+    for i in range(max(1, args.warmup)):
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+    log("[bench] layer warmup done")
+    lh.lh_timing_begin()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    st, stages = lh.lh_timing_end()
+    if st:
+        raise lh.LighthouseError(st, "lh_timing_end")
+    fl = layer_flops(B * N, dm, H * d)
+    out = {"ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3), "d_model": dm, "stages": {}}
+    for n, (tm, c) in stages.items():
+        rec = {"ms_per_step": tm / args.steps}
+        if n in fl and tm > 0:
+            rec["tflops"] = fl[n] / (tm / args.steps * 1e-3) / 1e12
+        out["stages"][n] = rec
+        log(f"[bench]   layer {n:14s} {rec['ms_per_step']:8.3f} ms/step" +
+            (f"  {rec['tflops']:7.1f} TFLOP/s" if "tflops" in rec else ""))
+    log(f"[bench] layer fwd+bwd: {ms:.3f} ms/step, {out['tokens_per_s']:.4g} tokens/s")
+    del saved, fws, bws, y, dx, dws, t
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +189,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="512k")
     ap.add_argument("--dense", action="store_true", help="also time dense causal attention at S = N")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time the projection-inclusive layer (W_Q, W_K, W_V, W_O around the attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps (a known-size "
@@ -254,6 +330,10 @@ def main() -> int:
         extra["lighthouse_step_speedup_vs_dense"] = (fms + bms) / ms
         log(f"[bench] dense causal attention at S=N: forward {fms:.1f} ms, backward {bms:.1f} ms")
         del od, lsed, grads, wsd
+
+    if args.layer:
+        del o, dq, dk, dv
+        extra["layer"] = time_layer(lh, synth, cfg, args, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

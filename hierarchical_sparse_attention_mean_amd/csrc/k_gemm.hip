@@ -49,15 +49,44 @@ constexpr int kGFillOps = 4;                   // 1 KB loads per wavefront per s
 constexpr int kGGroup = 4;                     // m-tiles an XCD walks together over all n-tiles
 static_assert(kGOpBytes / 1024 == 2 * (kGThreads / 64), "two 1 KB blocks per wavefront per operand");
 
+// A view's three base pointers as wave-uniform values: held in scalar
+// registers, so that choosing one per stage is a select, not a reload from the
+// kernel arguments (a scalar load, whose wait would also wait for every LDS read
+// in flight).
+// A pointer that is the same in every lane, as a scalar-register value (the
+// compiler may form uniform 64-bit address arithmetic on the vector ALUs; the
+// DMA's base operand must be scalar registers).
+__device__ __forceinline__ const char *uniform_ptr(const void *q) {
+  const unsigned long long a = (unsigned long long)q;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return reinterpret_cast<const char *>(((unsigned long long)hi << 32) | lo);
+}
+
+// (Three members rather than an array: an array indexed by a computed value
+// would be placed in scratch memory.)
+struct Bases {
+  const char *p0, *p1, *p2;
+  __device__ __forceinline__ explicit Bases(const MatView &v)
+      : p0(uniform_ptr(v.p[0])), p1(uniform_ptr(v.p[1])), p2(uniform_ptr(v.p[2])) {}
+  __device__ __forceinline__ const char *pick(unsigned which) const {
+    return which == 0 ? p0 : which == 1 ? p1 : p2;
+  }
+};
+
+// The global-memory address space, so that stores through computed pointers are
+// global stores (not flat ones, which would also count as LDS operations).
+typedef __attribute__((address_space(1))) char gchar;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Byte pointer of view element (r, c) of batch element b (c inside one column
 // block of the view; all arguments the same in every lane).
 template <int ES>
-__device__ __forceinline__ const char *vptr(const MatView &v, int b, long long r, unsigned c) {
+__device__ __forceinline__ const char *vptr(const MatView &v, const Bases &bs, int b, long long r, unsigned c) {
   const unsigned which = c / (unsigned)v.seg, cc = c - which * (unsigned)v.seg;
   const unsigned h = cc / (unsigned)v.hd, j = cc - h * (unsigned)v.hd;
-  const void *p = which == 0 ? v.p[0] : which == 1 ? v.p[1] : v.p[2];
-  return reinterpret_cast<const char *>(p) + (long long)ES * ((long long)b * v.bstride + (long long)h * v.hstride +
-                                                              r * v.ld + (long long)j);
+  return bs.pick(which) + (long long)ES * ((long long)b * v.bstride + (long long)h * v.hstride + r * v.ld + (long long)j);
 }
 
 // Per-lane byte offset, in a tile of W-byte bf16 rows, of the transposing read
@@ -86,16 +115,19 @@ __device__ __forceinline__ bf16x8 tr_seq(const char *tile, int lo, int hi) {
 // NB = fragments per k16 step (2 for A: 64 m per wavefront; 4 for B: 128 n).
 template <bool KM, int NB>
 struct Operand {
+  Bases bs;
   unsigned voff[2];      // per-lane source offset of each block (k-major: fixed; mn-major: without the k-tail clamp)
   int rrow[2];           // mn-major: tile row (k) of this lane in each block
   unsigned lc16[2];      // mn-major: 16 * logical chunk of this lane in each block
   const char *colbase[2];   // mn-major: base of the sub-tile's columns (k = 0)
   int frag[2][NB][2];    // LDS offsets of the fragment reads [kk][block][lo/hi]
 
-  // w: wavefront, mn0: first m (or n) of the tile, MN: its extent, wpos: first
-  // m (or n) of this wavefront's fragments inside the tile
-  __device__ __forceinline__ void init(const MatView &v, int b, int w, int mn0, int MN, int wpos) {
-    const int l = threadIdx.x & 63, ln = l & 31, hf = l >> 5;
+  __device__ __forceinline__ explicit Operand(const MatView &v) : bs(v) {}
+
+  // Sources of this wavefront's fills for a tile: w = wavefront, mn0 = first m
+  // (or n) of the tile, MN = its extent.
+  __device__ __forceinline__ void init_fill(const MatView &v, int b, int w, int mn0, int MN) {
+    const int l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = w + 8 * i;
@@ -110,9 +142,15 @@ struct Operand {
         rrow[i] = r;
         lc16[i] = 16u * (unsigned)((l & 7) ^ tiles::swz<128>(r));
         const int c0 = min(mn0 + 64 * s, MN - 64);              // sub-tiles past the extent repeat the last
-        colbase[i] = vptr<2>(v, b, 0, (unsigned)c0);
+        colbase[i] = vptr<2>(v, bs, b, 0, (unsigned)c0);
       }
     }
+  }
+
+  // LDS offsets of this lane's fragment reads; wpos = first m (or n) of the
+  // wavefront's fragments inside the tile (the same for every tile).
+  __device__ __forceinline__ void init_frag(int wpos) {
+    const int l = threadIdx.x & 63, ln = l & 31, hf = l >> 5;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -133,7 +171,7 @@ struct Operand {
   // k0 .. k0 + 31 (rows >= kend repeat row kend - 1) into LDS tile `dst`.
   __device__ __forceinline__ void fill(const MatView &v, int b, int mn0, int k0, int kend, char *dst, int w) {
     if constexpr (KM) {
-      const char *base = vptr<2>(v, b, mn0, (unsigned)k0);
+      const char *base = uniform_ptr(vptr<2>(v, bs, b, mn0, (unsigned)k0));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         tiles::lds_load_s<16>(base, voff[i], tiles::lds_addr(dst + 1024 * (w + 8 * i)));
@@ -141,7 +179,7 @@ struct Operand {
       const int kmax = kend - 1 - k0;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const char *base = colbase[i] + 2LL * k0 * v.ld;
+        const char *base = uniform_ptr(colbase[i] + 2LL * k0 * v.ld);
         const unsigned off = (unsigned)(min(rrow[i], kmax) * v.ld * 2) + lc16[i];
         tiles::lds_load_s<16>(base, off, tiles::lds_addr(dst + 1024 * (w + 8 * i)));
       }
@@ -156,7 +194,80 @@ struct Operand {
 
 template <bool B> struct Flag { static constexpr bool value = B; };
 
-// AKM / BKM: A / B k-major.  OUT: lh_dtype of C.
+// One stage (32 contraction steps) of a wavefront's 128 x 64 block: operands
+// from ring slot `ta`; kstage = first contraction index of the stage.  TAIL:
+// the stage reaches past kend, whose A entries (repeats) are zeroed.
+template <bool TAIL, bool AKM, bool BKM>
+__device__ __forceinline__ void mfma_stage(f32x16 (&acc)[4][2], const Operand<AKM, 2> &A, const Operand<BKM, 4> &Bo,
+                                           const char *ta, int kstage, int kend) {
+  const char *tb = ta + kGOpBytes;
+  const int hf = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 af[2], bfr[4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) af[f] = A.read(ta, kk, f);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bfr[f] = Bo.read(tb, kk, f);
+    if constexpr (TAIL) {
+      const int kfirst = kstage + 16 * kk + 8 * hf;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kfirst + e >= kend) af[f][e] = (__bf16)0.f;
+    }
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fn][fm], 0, 0, 0);
+  }
+}
+
+// Stores of a wavefront's block.  D[n][m] = C[m][n]: lane (ln, hf) of fragment
+// (fn, fm) holds m = m0 + 64 wm + 32 fm + ln and n = n0 + 128 wn + 32 fn + 8 q +
+// 4 hf + 0..3 in acc[fn][fm][4 q .. 4 q + 3].  FULL: the tile lies inside C.
+template <int OUT, bool FULL>
+__device__ __forceinline__ void store_block(const f32x16 (&acc)[4][2], const GemmArgs &g, int b, int z, int m0, int n0,
+                                            int wm, int wn) {
+  const int l = threadIdx.x & 63, ln = l & 31, hf = l >> 5;
+  constexpr int ES = OUT == LH_BF16 ? 2 : 4;
+  const Bases cb(g.c);
+#pragma unroll
+  for (int fn = 0; fn < 4; ++fn) {
+    const int nb = n0 + 128 * wn + 32 * fn;
+    if (!FULL && nb >= g.N) continue;
+    gchar *base = (gchar *)(vptr<ES>(g.c, cb, b, 0, (unsigned)nb)) + (long long)ES * z * g.zstride;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm) {
+      const int m = m0 + 64 * wm + 32 * fm + ln;
+      if (!FULL && m >= g.M) continue;
+      gchar *row = base + (long long)ES * ((long long)m * g.c.ld + 4 * hf);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16 &a = acc[fn][fm];
+        if constexpr (OUT == LH_BF16) {
+          const unsigned lo = f32_to_bf16_rne(a[4 * q]) | ((unsigned)f32_to_bf16_rne(a[4 * q + 1]) << 16);
+          const unsigned hi = f32_to_bf16_rne(a[4 * q + 2]) | ((unsigned)f32_to_bf16_rne(a[4 * q + 3]) << 16);
+          *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(row + 2 * 8 * q) = (u32x2){lo, hi};
+        } else {
+          *reinterpret_cast<__attribute__((address_space(1))) f32x4 *>(row + 4 * 8 * q) =
+              (f32x4){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void zero(f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+}
+
+// One work-group per tile.  AKM / BKM: A / B k-major.  OUT: lh_dtype of C.
 template <bool AKM, bool BKM, int OUT>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_mfma(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds[kGStages * kGStageBytes];
@@ -184,16 +295,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_mfma(GemmArgs g) {
   const int kbeg = z * g.kchunk, kend = min(g.K, kbeg + g.kchunk);
   const int nk = kend > kbeg ? (kend - kbeg + kGBK - 1) / kGBK : 0;
 
-  Operand<AKM, 2> A;
-  Operand<BKM, 4> Bo;
-  A.init(g.a, b, w, m0, g.M, 64 * wm);
-  Bo.init(g.b, b, w, n0, g.N, 128 * wn);
-
+  Operand<AKM, 2> A(g.a);
+  Operand<BKM, 4> Bo(g.b);
+  A.init_fill(g.a, b, w, m0, g.M);
+  A.init_frag(64 * wm);
+  Bo.init_fill(g.b, b, w, n0, g.N);
+  Bo.init_frag(128 * wn);
   f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+  zero(acc);
 
   auto fill = [&](int t) {   // stage t (clamped to the last) into ring slot t % kGStages
     const int k0 = kbeg + kGBK * min(t, nk - 1);
@@ -201,35 +310,6 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_mfma(GemmArgs g) {
     A.fill(g.a, b, m0, k0, kend, dst, w);
     Bo.fill(g.b, b, n0, k0, kend, dst + kGOpBytes, w);
   };
-
-  const int l = threadIdx.x & 63, hf = l >> 5;
-  auto stage = [&](int t, auto tail) {
-    constexpr bool TAIL = decltype(tail)::value;
-    const char *ta = lds + (t % kGStages) * kGStageBytes;
-    const char *tb = ta + kGOpBytes;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[2], bfr[4];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) af[f] = A.read(ta, kk, f);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) bfr[f] = Bo.read(tb, kk, f);
-      if constexpr (TAIL) {   // contraction indices >= kend: A's entries are repeats, zero them
-        const int kfirst = kbeg + kGBK * t + 16 * kk + 8 * hf;
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kfirst + e >= kend) af[f][e] = (__bf16)0.f;
-      }
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < 2; ++fm)
-          acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fn][fm], 0, 0, 0);
-    }
-  };
-
   if (nk > 0) {
     fill(0);
     fill(1);
@@ -239,40 +319,13 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_mfma(GemmArgs g) {
     const int nfull = tail ? nk - 1 : nk;
     for (int t = 0; t < nfull; ++t) {
       fill(t + 3);   // ring slot of stage t - 1, which every wavefront has finished
-      stage(t, Flag<false>{});
+      mfma_stage<false>(acc, A, Bo, lds + (t % kGStages) * kGStageBytes, kbeg + kGBK * t, kend);
       tiles::wait_fills_barrier<2 * kGFillOps>();
     }
-    if (tail) stage(nk - 1, Flag<true>{});
+    if (tail) mfma_stage<true>(acc, A, Bo, lds + ((nk - 1) % kGStages) * kGStageBytes, kbeg + kGBK * (nk - 1), kend);
     tiles::dma_wait();   // the fills past the last stage
   }
-
-  // D[n][m] = C[m][n]: lane (ln, hf) of fragment (fn, fm) holds m = m0 + 64 wm + 32 fm + ln and
-  // n = n0 + 128 wn + 32 fn + 8 q + 4 hf + 0..3 in acc[fn][fm][4 q .. 4 q + 3]
-  const int ln = l & 31;
-  constexpr int ES = OUT == LH_BF16 ? 2 : 4;
-#pragma unroll
-  for (int fn = 0; fn < 4; ++fn) {
-    const int nb = n0 + 128 * wn + 32 * fn;
-    if (nb >= g.N) continue;
-    char *base = const_cast<char *>(vptr<ES>(g.c, b, 0, (unsigned)nb)) + (long long)ES * z * g.zstride;
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-      const int m = m0 + 64 * wm + 32 * fm + ln;
-      if (m >= g.M) continue;
-      char *row = base + (long long)ES * ((long long)m * g.c.ld + 4 * hf);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16 &a = acc[fn][fm];
-        if constexpr (OUT == LH_BF16) {
-          const unsigned lo = f32_to_bf16_rne(a[4 * q]) | ((unsigned)f32_to_bf16_rne(a[4 * q + 1]) << 16);
-          const unsigned hi = f32_to_bf16_rne(a[4 * q + 2]) | ((unsigned)f32_to_bf16_rne(a[4 * q + 3]) << 16);
-          *reinterpret_cast<uint2 *>(row + 2 * 8 * q) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4 *>(row + 4 * 8 * q) = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-        }
-      }
-    }
-  }
+  store_block<OUT, false>(acc, g, b, z, m0, n0, wm, wn);
 }
 
 // ---------------------------------------------------------------------------

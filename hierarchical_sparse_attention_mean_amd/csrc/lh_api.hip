@@ -251,12 +251,25 @@ void layer_layout(const lh::Shape &s, int d_model, lh_layer_layout_t *o) {
   o->total = cur;
 }
 
-// Weight gradients contract over the N tokens of each batch element: split the
-// contraction so that the product has about 1024 work-groups; partials are
-// [B][splits][M][N] fp32.
-void wgrad_split(int M, int Nc, int64_t N, int io, int *splits, int *kchunk) {
+// Weight gradients contract over the N tokens of each batch element, so the
+// product is split along the tokens; partials are [B][splits][M][N] fp32.
+// bf16: splits = 8 n (each XCD runs n of them) into equal chunks of whole
+// 32-token stages, with the work-groups of an XCD (n x tiles x B) a multiple of
+// its 32 compute units and at least two per unit, so that every compute unit
+// gets the same work; failing that, about 1024 work-groups.
+void wgrad_split(int M, int Nc, int64_t N, int B, int io, int *splits, int *kchunk) {
   const int tm = io == LH_BF16 ? 256 : 64;
   const int64_t tiles = ((M + tm - 1) / tm) * (int64_t)((Nc + tm - 1) / tm);
+  if (io == LH_BF16) {
+    for (int n = 1; n <= 64; ++n) {
+      const int64_t sp = 8 * n, items = n * tiles * B;
+      if (N % sp == 0 && (N / sp) % 32 == 0 && items % 32 == 0 && items >= 64) {
+        *splits = (int)sp;
+        *kchunk = (int)(N / sp);
+        return;
+      }
+    }
+  }
   const int64_t target = tiles >= 1024 ? 1 : 1024 / tiles;
   int64_t kc = (N + target - 1) / target;
   kc = (kc + 31) / 32 * 32;
@@ -290,8 +303,8 @@ void layer_bwd_layout(const lh::Shape &s, int B, int H, int d_model, LayerBwdWs 
   w->inner = take(bw.total);
   w->inner_bytes = bw.total;
   const int Hd = H * s.d;
-  wgrad_split(d_model, 3 * Hd, s.N, s.io, &w->split_qkv, &w->kchunk_qkv);
-  wgrad_split(Hd, d_model, s.N, s.io, &w->split_o, &w->kchunk_o);
+  wgrad_split(d_model, 3 * Hd, s.N, B, s.io, &w->split_qkv, &w->kchunk_qkv);
+  wgrad_split(Hd, d_model, s.N, B, s.io, &w->split_o, &w->kchunk_o);
   const size_t pq = (size_t)B * w->split_qkv * (size_t)d_model * 3 * Hd;
   const size_t po = (size_t)B * w->split_o * (size_t)Hd * d_model;
   w->part = take(4 * (pq > po ? pq : po));
