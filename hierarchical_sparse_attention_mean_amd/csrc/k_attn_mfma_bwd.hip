@@ -22,13 +22,11 @@
 //                    work-group (the accumulators need the register file of a
 //                    whole SIMD).
 // Both stream their tiles through LDS filled by direct global->LDS loads
-// (attn_tiles.h) while earlier tiles are computed; dK/dV software-pipelines
-// the S/dP products of tile t+1 with the softmax of tile t (three buffers).  The
-// transposed operands (K~^T, Q~^T, dO~^T; row stride Sv, a multiple of 64,
-// zero padded, columns in perm16 order) are written by the gather and by the
-// scatter adjoint, so every LDS operand is one 16-byte read per lane.  The
-// row-major operands are padded with zero rows up to Sv, so no tile load needs a
-// bounds check: a padding query or key contributes exactly 0.
+// (attn_tiles.h) while earlier tiles are computed.  Operands contracted over
+// keys or queries (K~^T, Q~^T, dO~^T) come from the row-major tiles by
+// transposing LDS reads.  The row-major operands are padded with zero rows up
+// to Sv (a multiple of 64), so no tile load needs a bounds check: a padding
+// query or key contributes exactly 0.
 #include "attn_tiles.h"
 
 namespace lh {
@@ -343,26 +341,26 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   fill(1, min(j0 + kKvBQ, qlast));
   tiles::wait_fills_barrier<kFillOps>();   // tile 0 landed
 
-  // 32x32 product over d: rows of a row-major tile (A operand) times this
-  // lane's key row (B operand)
-  auto rowprod = [&](const char *tile) {
-    bf16x8 f[KC];
+  // fragment reads of a phase are all issued before its first product, so
+  // the LDS latency is paid once per phase rather than once per product
+  auto rowfr = [&](const char *tile, bf16x8 (&f)[KC]) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) f[c] = tiles::lds_frag(tile, oq[c]);
-    f32x16 r = (f32x16){};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], kv[c], r, 0, 0, 0);
-    return r;
   };
-  // acc^T += X^T x for a row-major tile X (rows = the tile's queries) and the
-  // bf16 B operand chunks x[cc] (16 queries each, probability-register order)
-  auto colprod = [&](const char *tile, const bf16x8 *x) {
-    bf16x8 f[KC];
+  auto colfr = [&](const char *tile, bf16x8 (&f)[KC]) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const int cc = c / DB, b = c % DB;
       f[c] = tiles::tr_frag(tile + 16 * cc * T::WR, otr[b][0], otr[b][1]);
     }
+  };
+  auto rowmm = [&](const bf16x8 (&f)[KC]) {
+    f32x16 r = (f32x16){};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], kv[c], r, 0, 0, 0);
+    return r;
+  };
+  auto colmm = [&](const bf16x8 (&f)[KC], const bf16x8 *x) {
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       acc[c % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], x[c / DB], acc[c % DB], 0, 0, 0);
@@ -375,10 +373,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
       const int q0 = j0 + t * kKvBQ;
       const char *cur = lds + (t % kKvBufs) * T::BYTES;
       fill((t + 2) % kKvBufs, min(q0 + 2 * kKvBQ, qlast));   // past the end: a repeat of the last tile
+      bf16x8 fq[KC], fg[KC];
+      rowfr(cur + T::Q, fq);
       float4 l4[4];   // LSE log2 e of rows 8 g4 + 4 hf + 0..3
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) l4[g4] = *reinterpret_cast<const float4 *>(cur + T::LS + 4 * (8 * g4 + 4 * hf));
-      const f32x16 sv = rowprod(cur + T::Q);
+      colfr(cur + T::G, fg);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16 sv = rowmm(fq);
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
       bf16x8 pf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = (__bf16)p[i];
-      colprod(cur + T::G, pf);   // dV~^T += dO~^T P
+      colmm(fg, pf);   // dV~^T += dO~^T P
       tiles::wait_fills_barrier<kFillOps>();   // tile t+1 landed
     };
     const int nm = min(nt, kKvBK / kKvBQ);   // tiles that reach below some key of the block: masked
@@ -405,15 +407,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   } else {
     // ---- dS wavefront: dP of tile t; dS and dK of tile t-1 ----
     f32x16 dpp = (f32x16){};   // dP of the previous tile
-    auto ds_dk = [&](int t) {   // dS and dK~ of tile t (its P in the exchange)
-      const char *tb = lds + (t % kKvBufs) * T::BYTES;
-      const char *x = xch + (t & 1) * (kKvPairs * kXBytes) + ox;
-      float4 p4[4], d4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p4[k] = *reinterpret_cast<const float4 *>(x + 1024 * k);
-        d4[k] = *reinterpret_cast<const float4 *>(tb + T::DL + 4 * (8 * k + 4 * hf));
-      }
+    auto ds_dk = [&](int t, const bf16x8 (&fq)[KC], const float4 (&p4)[4], const float4 (&d4)[4]) {
       bf16x8 dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -422,17 +416,37 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
         const float dl = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
         dsf[i >> 3][i & 7] = (__bf16)(pj * (dpp[i] - dl));
       }
-      colprod(tb + T::Q, dsf);   // dK~^T += Q~^T dS
+      colmm(fq, dsf);   // dK~^T += Q~^T dS
+    };
+    auto ds_reads = [&](int t, bf16x8 (&fq)[KC], float4 (&p4)[4], float4 (&d4)[4]) {
+      const char *tb = lds + (t % kKvBufs) * T::BYTES;
+      const char *x = xch + (t & 1) * (kKvPairs * kXBytes) + ox;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        p4[k] = *reinterpret_cast<const float4 *>(x + 1024 * k);
+        d4[k] = *reinterpret_cast<const float4 *>(tb + T::DL + 4 * (8 * k + 4 * hf));
+      }
+      colfr(tb + T::Q, fq);
     };
     for (int t = 0; t < nt; ++t) {
       const int q0 = j0 + t * kKvBQ;
       const char *cur = lds + (t % kKvBufs) * T::BYTES;
       fill((t + 2) % kKvBufs, min(q0 + 2 * kKvBQ, qlast));
-      if (t > 0) ds_dk(t - 1);
-      dpp = rowprod(cur + T::G);   // dP = dO~ V~^T
+      bf16x8 fq[KC], fg[KC];
+      float4 p4[4], d4[4];
+      if (t > 0) ds_reads(t - 1, fq, p4, d4);
+      rowfr(cur + T::G, fg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t > 0) ds_dk(t - 1, fq, p4, d4);
+      dpp = rowmm(fg);   // dP = dO~ V~^T
       tiles::wait_fills_barrier<kFillOps>();
     }
-    ds_dk(nt - 1);
+    {
+      bf16x8 fq[KC];
+      float4 p4[4], d4[4];
+      ds_reads(nt - 1, fq, p4, d4);
+      ds_dk(nt - 1, fq, p4, d4);
+    }
   }
   tiles::dma_wait();   // the fills past the last tile, before the work-group exits
 

@@ -89,6 +89,7 @@ def test_backward_8k_select_all(lh):
 def test_backward_shapes(lh):
     _run_bwd(lh, synth.config("tiny", N=2048, L=4, p=2, k=13, B=2, H=1, d=128), heads=[0, 1])
     _run_bwd(lh, synth.config("tiny", N=1552, L=3, p=4, k=40, H=1), heads=[0], grad_dtype="bf16")
+    _run_bwd(lh, synth.config("tiny", N=1944, L=3, p=3, k=20, H=1), heads=[0])   # p not a power of two
 
 
 def test_backward_properties_scale_and_determinism(lh):

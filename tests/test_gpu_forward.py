@@ -145,6 +145,7 @@ def test_tiny_L1_dense(lh):
     (3072, 2, 4, 5, 1, 3),      # two levels
     (512, 3, 2, 0, 1, 1),       # k = 0: only the coarsest level
     (4096, 5, 2, 200, 1, 1),    # five levels
+    (1944, 3, 3, 20, 1, 2),     # p = 3: a pooling factor that is not a power of two
 ])
 def test_shapes_fp32(lh, N, L, p, k, B, H):
     cfg = synth.config("tiny", N=N, L=L, p=p, k=k, B=B, H=H, recipe="mod97x4")
@@ -204,11 +205,14 @@ def test_deterministic(lh):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
 
 
-def test_scatter_large_values(lh):
+@pytest.mark.parametrize("N,L,p", [(1024, 3, 4), (1944, 3, 3)])
+def test_scatter_large_values(lh, N, L, p):
     """Sub-sequence outputs of magnitude >= 2^18 make the scatter form its
     fixed-point sums in int64 instead of fp64; the result stays bit-exact.
-    V is scaled by 2^20 on half of the positions, so both forms occur."""
-    cfg = synth.config("tiny")
+    V is scaled by 2^20 on half of the positions, so both forms occur.  p = 4
+    and p = 3 take the scatter's two thread layouts (groups of four positions
+    sharing their coarser entries, one position per thread)."""
+    cfg = synth.config("tiny", N=N, L=L, p=p)
     inp = synth.make_inputs(cfg)
     N, L, p = cfg["N"], cfg["L"], cfg["p"]
     inp["v"] = inp["v"].copy()
