@@ -15,10 +15,12 @@
 // the joint selection over the concatenated QK || KQ stream.
 //
 // Work mapping: a work-group of 256 threads covers RG row-groups x CH column
-// chunks (8 elements each).  Row-group rg owns one coarsest window of
-// G = p^(L-1) consecutive rows and walks it top to bottom, so every pooled
-// window and every max-pool lives in one thread's registers; only the norm of a
-// row needs a reduction, across the CH lanes that hold it (adjacent lanes of one
+// chunks of EL elements (EL = 8 up to three levels, 4 beyond, which halves the
+// per-level accumulators so that more wavefronts fit).  Row-group rg owns one
+// coarsest window of G = p^(L-1) consecutive rows and walks it top to bottom,
+// reading each row one step ahead of its use, so every pooled window and every
+// max-pool lives in one thread's registers; only the norm of a row needs a
+// reduction, across the CH lanes that hold it (adjacent lanes of one
 // wavefront, reduced with xor shuffles).
 #include "lh_internal.h"
 
@@ -27,6 +29,28 @@ namespace lh {
 namespace {
 
 constexpr int kMaxL = 8;   // most levels handled by the register-resident accumulators
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float *p, float (&x)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
+  static __device__ __forceinline__ void store(float *p, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+template <> struct Vec4<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t *p, float (&x)[4]) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    x[0] = __uint_as_float(a.x << 16); x[1] = __uint_as_float(a.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(a.y << 16); x[3] = __uint_as_float(a.y & 0xFFFF0000u);
+  }
+  static __device__ __forceinline__ void store(uint16_t *p, const float (&x)[4]) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2((unsigned)f32_to_bf16_rne(x[0]) | ((unsigned)f32_to_bf16_rne(x[1]) << 16),
+                                               (unsigned)f32_to_bf16_rne(x[2]) | ((unsigned)f32_to_bf16_rne(x[3]) << 16));
+  }
+};
 
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
@@ -59,6 +83,10 @@ template <> struct Vec8<uint16_t> {
   }
 };
 
+template <typename T, int N> struct VecN;
+template <typename T> struct VecN<T, 4> : Vec4<T> {};
+template <typename T> struct VecN<T, 8> : Vec8<T> {};
+
 __device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f, int P) {
   const float r = fmaxf(qk, kq);
   const unsigned int g = (qk >= kq) ? (unsigned int)f : (unsigned int)(P + f);
@@ -69,7 +97,8 @@ template <typename T, int D, int ML>
 __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v, char *__restrict__ ws, FwdWs w,
                                                     float *__restrict__ scores) {
-  constexpr int CH = D / 8;          // threads per row
+  constexpr int EL = ML <= 3 ? 8 : 4;   // elements per lane
+  constexpr int CH = D / EL;         // threads per row
   constexpr int RG = 256 / CH;       // row-groups per work-group
   const int h = blockIdx.y;
   const int j = threadIdx.x % CH;
@@ -86,32 +115,45 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   unsigned long long *keys = reinterpret_cast<unsigned long long *>(ws + w.keys) + (long long)h * s.E;
 
   // running window sums and max-pooled scores per level l >= 1 (ML >= L levels)
-  float aq[ML][8], ak[ML][8], av[ML][8];
+  float aq[ML][EL], ak[ML][EL], av[ML][EL];
   float ma[ML], mb[ML];
 #pragma unroll
   for (int l = 0; l < ML; ++l) {
     ma[l] = 0.f;
     mb[l] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
+    for (int e = 0; e < EL; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
   }
   unsigned int umin = 0xFFFFFFFFu, umax = 0u;
 
   const long long t0 = win * G;
+  // the rows of the window are read one ahead of their use
+  const long long last = active ? t0 + G - 1 : 0;
+  float nq[EL], nk[EL], nv[EL];
+  {
+    const long long t = active ? t0 : 0;
+    VecN<T, EL>::load(q + hoff + t * D + j * EL, nq);
+    VecN<T, EL>::load(k + hoff + t * D + j * EL, nk);
+    VecN<T, EL>::load(v + hoff + t * D + j * EL, nv);
+  }
   for (int r = 0; r < G; ++r) {
     const long long t = t0 + r;
-    float xq[8], xk[8], xv[8];
-    if (active) {
-      Vec8<T>::load(q + hoff + t * D + j * 8, xq);
-      Vec8<T>::load(k + hoff + t * D + j * 8, xk);
-      Vec8<T>::load(v + hoff + t * D + j * 8, xv);
-    } else {
+    float xq[EL], xk[EL], xv[EL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.f;
+    for (int e = 0; e < EL; ++e) {
+      xq[e] = active ? nq[e] : 0.f;
+      xk[e] = active ? nk[e] : 0.f;
+      xv[e] = active ? nv[e] : 0.f;
+    }
+    {
+      const long long tn = active ? min(t + 1, last) : 0;
+      VecN<T, EL>::load(q + hoff + tn * D + j * EL, nq);
+      VecN<T, EL>::load(k + hoff + tn * D + j * EL, nk);
+      VecN<T, EL>::load(v + hoff + tn * D + j * EL, nv);
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < EL; ++e) {
       sq = fmaf(xq[e], xq[e], sq);
       sk = fmaf(xk[e], xk[e], sk);
     }
@@ -136,7 +178,7 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
     if (L == 1) continue;
     // level 1 accumulates rows; level l+1 accumulates completed level-l windows
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < EL; ++e) {
       aq[1][e] += xq[e];
       ak[1][e] += xk[e];
       av[1][e] += xv[e];
@@ -150,17 +192,17 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
       const long long i = (t + 1) / s.pw[l] - 1;
       const float inv = 1.0f / (float)s.pw[l];
       if (active) {
-        float mq[8], mk[8], mv[8];
+        float mq[EL], mk[EL], mv[EL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < EL; ++e) {
           mq[e] = aq[l][e] * inv;
           mk[e] = ak[l][e] * inv;
           mv[e] = av[l][e] * inv;
         }
-        const long long lo = ((long long)h * s.n[l] + i) * D + j * 8;
-        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][0]) + lo, mq);
-        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][1]) + lo, mk);
-        Vec8<T>::store(reinterpret_cast<T *>(ws + w.lev[l][2]) + lo, mv);
+        const long long lo = ((long long)h * s.n[l] + i) * D + j * EL;
+        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][0]) + lo, mq);
+        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][1]) + lo, mk);
+        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][2]) + lo, mv);
         if (j == 0) {
           const int f = s.off[l] + (int)i;
           sc_qk[f] = ma[l];
@@ -176,7 +218,7 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
       }
       if (l + 1 < ML && l + 1 < L) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < EL; ++e) {
           aq[l + 1][e] += aq[l][e];
           ak[l + 1][e] += ak[l][e];
           av[l + 1][e] += av[l][e];
@@ -185,7 +227,7 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
         mb[l + 1] = fmaxf(mb[l + 1], mb[l]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
+      for (int e = 0; e < EL; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
       ma[l] = 0.f;
       mb[l] = 0.f;
     }
@@ -242,7 +284,7 @@ static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                              const FwdWs &w, float *scores, hipStream_t st) {
   if (s.L > kMaxL) return hipErrorInvalidValue;
-  const int CH = s.d / 8;
+  const int CH = s.d / (s.L <= 3 ? 8 : 4);   // elements per lane as in the kernel (ML <= 3: 8)
   const int RG = 256 / CH;
   const int nwin = s.n[s.L - 1];
   dim3 grid((nwin + RG - 1) / RG, s.BH);

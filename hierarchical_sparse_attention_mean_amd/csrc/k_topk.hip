@@ -18,9 +18,12 @@
 //                     it are appended to a per-head candidate list.
 //   3. k_topk_refine  one work-group per head takes the `need` largest of the
 //                     candidates: radix passes over the list while it is larger
-//                     than LDS, then a bitonic sort staged in registers (in-thread
-//                     and cross-lane shuffle stages) and LDS (cross-wave stages).
+//                     than LDS, else a bitonic sort of the next power-of-two size
+//                     staged in registers (in-thread and cross-lane shuffle stages)
+//                     and LDS (cross-wave stages).
 // Flags of the coarsest level are set to 1 by the filter.
+#include <type_traits>
+
 #include "lh_internal.h"
 
 namespace lh {
@@ -235,21 +238,29 @@ __global__ __launch_bounds__(kRefineThreads) void k_topk_refine(Shape s, char *_
     for (long long i = tid; i < C; i += kRefineThreads) fl[key_flat(cand[i], s.P)] = 1;
     return;
   }
-  if (C <= kTopkCandLds) {
-    unsigned long long x[PER];
+  // the candidates, padded with zeros to the next sort size (1024 .. kTopkCandLds
+  // keys: one to PER per thread), sorted in registers and LDS; the first
+  // `need` are selected
+  auto sort_select = [&](auto per) {
+    constexpr int R = decltype(per)::value;
+    unsigned long long x[R];
 #pragma unroll
-    for (int sl = 0; sl < PER; ++sl) {
+    for (int sl = 0; sl < R; ++sl) {
       const long long e = (long long)sl * kRefineThreads + tid;
       x[sl] = e < C ? cand[e] : 0ull;   // 0 is below every real key (its low half is never 0)
     }
-    bitonic_sort_desc<kRefineThreads, PER>(x, lds);
+    bitonic_sort_desc<kRefineThreads, R>(x, lds);
 #pragma unroll
-    for (int sl = 0; sl < PER; ++sl) {
+    for (int sl = 0; sl < R; ++sl) {
       const long long e = (long long)sl * kRefineThreads + tid;
       if (e < need) fl[key_flat(x[sl], s.P)] = 1;
     }
-    return;
-  }
+  };
+  static_assert(PER == 8, "sort sizes below");
+  if (C <= kRefineThreads) return sort_select(std::integral_constant<int, 1>{});
+  if (C <= 2 * kRefineThreads) return sort_select(std::integral_constant<int, 2>{});
+  if (C <= 4 * kRefineThreads) return sort_select(std::integral_constant<int, 4>{});
+  if (C <= kTopkCandLds) return sort_select(std::integral_constant<int, 8>{});
   // Radix select of the need-th largest key over the list in global memory:
   // 8-bit digits from the top; keys are unique, so the threshold is exact.
   unsigned long long prefix = 0, mask = 0;
