@@ -172,6 +172,51 @@ def test_ties_everywhere(lh):
     assert np.array_equal(np.nonzero(g["flags"][:cfg["N"] + cfg["N"] // 4])[0], np.arange(E))
 
 
+def _boundary_candidates(qk_flat, kq_flat, N, L, p, topk):
+    """Keys in the top-k's boundary histogram bin, from the GPU's own scores:
+    the same 12-bit digit of the score bits over the per-head [min, max]
+    range that the kernels use (coverage probe for the refine paths)."""
+    n = [N // p ** l for l in range(L)]
+    E = sum(n[:-1])
+    bsel = min((L - 1) * p * topk, E)
+    hi = np.maximum(qk_flat[:E], kq_flat[:E]).astype(np.float32).view(np.uint32).astype(np.int64)
+    umin, umax = int(hi.min()), int(hi.max())
+    sh = 0
+    while ((umax - umin) >> sh) >= 4096:
+        sh += 1
+    hist = np.bincount((hi - umin) >> sh, minlength=4096)
+    above = np.cumsum(hist[::-1])[::-1] - hist   # keys in higher bins
+    b = int(np.nonzero((above < bsel) & (above + hist >= bsel))[0][0])
+    return int(hist[b])
+
+
+@pytest.mark.parametrize("frac,topk,lo,hi", [
+    (0.01, 16, 1, 1024),          # one key per thread
+    (0.05, 128, 1025, 2048),      # two
+    (0.10, 256, 2049, 4096),      # four
+    (0.20, 256, 4097, 8192),      # eight
+    (0.50, 256, 8193, 1 << 30),   # more than LDS holds: radix passes over the list
+])
+def test_topk_dense_boundary_bin(lh, frac, topk, lo, hi):
+    """Scores with two values only: Q_t = c_t u with c_t in {1, 2} (a seeded
+    fraction `frac` of rows get 2), K_t = u / 4, so every key's score is |u| or
+    2|u| exactly and the boundary bin holds every entry scoring 2|u|.  Its size
+    (checked from the GPU's scores) steers the refine through each of its sort
+    sizes and the radix path; the selection must still be bit-exact."""
+    cfg = synth.config("tiny", N=16384, H=1, k=topk)
+    inp = synth.make_inputs(cfg)
+    u = (np.linspace(0.5, 1.5, cfg["d"]) / 8).astype(np.float32)
+    c = np.where(np.random.default_rng(7).random(cfg["N"]) < frac, 2.0, 1.0).astype(np.float32)
+    inp["q"][0, 0] = c[:, None] * u[None, :]
+    inp["k"][0, 0] = u[None, :] / 4
+    run = run_forward(lh, cfg, inp)
+    g = gpu_head(lh, run, 0)
+    C = _boundary_candidates(g["qk_flat"], g["kq_flat"], cfg["N"], cfg["L"], cfg["p"], topk)
+    say(f"  boundary bin: {C} candidates")
+    assert lo <= C <= hi
+    check_head(cfg, inp, g, 0, cfg["L"], cfg["p"], topk, full_attention=False, sample_rows=128)
+
+
 def test_98k_bf16(lh):
     """98K training shape: every head's selection / order / scatter exact,
     attention and end-to-end on sampled rows."""
