@@ -6,7 +6,7 @@ backward, gather+pool adjoint) for one batch of seeded synthetic bf16 inputs
 already resident in HBM.  Default workload: B=1, H=8, d=128, N=524,288, L=3,
 p=4, k=4,096 (S=65,536).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--dense] [--layer]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--no-dense] [--layer]
 
 Prints one JSON line (rank 0).  Besides the contract fields it carries:
   roofline      the dominant kernel of the step (by time): its algorithmic FLOPs
@@ -17,8 +17,10 @@ Prints one JSON line (rank 0).  Besides the contract fields it carries:
                 when the kernel's sources changed since the counters were taken
   cpu_baseline  the fp64 oracle on one head of the same workload (fwd + bwd),
                 on this host's cores, scaled to the layer's tokens/s
-  extra         per-stage times, forward-only time, (with --dense) the dense
-                causal attention kernel at S = N, and (with --layer) the
+  extra         per-stage times (with algorithmic bytes and achieved GB/s for the
+                memory-bound stages), forward-only time, the dense causal
+                attention kernels at S = N (one forward and one backward; skipped
+                with --no-dense), and (with --layer) the
                 projection-inclusive layer (X -> W_Q, W_K, W_V -> Lighthouse ->
                 W_O, forward and backward) at d_model = 1024 with the TFLOP/s of
                 its four product stages
@@ -59,6 +61,28 @@ ATTN_STAGES = {
     "attn_bwd_dq": (3, ["k_attn_mfma_bwd.hip", "attn_tiles.h"]),
     "attn_bwd_dkdv": (4, ["k_attn_mfma_bwd.hip", "attn_tiles.h"]),
 }
+
+
+def hbm_stage_bytes(cfg: dict, S: int) -> dict:
+    """Algorithmic HBM bytes of the memory-bound stages for one step: what each
+    stage must read and write once (bf16 or fp32 storage of Q, K, V, O and the
+    gradients as the workload has it; O~, dQ~, dK~, dV~ in fp32; scores fp32;
+    keys 8 bytes; flags 1 byte; slot map and coordinates 4 bytes)."""
+    B, H, N, d, L, p = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["L"], cfg["p"]
+    BH = B * H
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    n = [N // p ** l for l in range(L)]
+    P, E = sum(n), sum(n[:-1])
+    Sv = (S + 63) // 64 * 64
+    r16, r32 = d * io, d * 4
+    return {
+        "pool_score": BH * (3 * N * r16 + 3 * sum(n[1:]) * r16 + 2 * P * 4 + E * 8),
+        "topk": BH * (2 * E * 8 + P),
+        "gather": BH * (2 * P + P * 4 + S * 4 + 2 * 3 * S * r16),
+        "scatter": BH * (S * r32 + P * 4 + N * r16),
+        "scatter_bwd": BH * (N * r16 + S * r32 + 2 * S * 4 + Sv * r16 + Sv * 8),
+        "pool_bwd": BH * (3 * S * r32 + P * 4 + 3 * N * r16),
+    }
 
 
 def sources_sha256(files) -> str:
@@ -188,7 +212,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="512k")
-    ap.add_argument("--dense", action="store_true", help="also time dense causal attention at S = N")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the dense causal attention kernels at S = N (one forward and one backward)")
     ap.add_argument("--layer", action="store_true",
                     help="also time the projection-inclusive layer (W_Q, W_K, W_V, W_O around the attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,10 +323,18 @@ def main() -> int:
         if rec["ms_per_launch"]:
             rec["tflops"] = attention_flops(S, d, BH, ATTN_STAGES[n][0]) / (rec["ms_per_launch"] * 1e-3) / 1e12
 
+    for n, nbytes in hbm_stage_bytes(cfg, S).items():
+        rec = stage_ms[n]
+        if rec["ms_per_step"] > 0:
+            rec["algorithmic_bytes"] = nbytes
+            rec["gbs"] = nbytes / (rec["ms_per_step"] * 1e-3) / 1e9
+            rec["frac_of_hbm_peak"] = rec["gbs"] / PEAK_HBM_GBS
+            log(f"[bench]   {n:14s} {rec['gbs']:8.0f} GB/s ({rec['frac_of_hbm_peak']:.0%} of {PEAK_HBM_GBS:.0f})")
+
     extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "stages": stage_ms,
              "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
     stream = torch.cuda.current_stream()
-    if args.dense:
+    if not args.no_dense:
         # the same attention kernels on the full sequence (S = N): dense causal attention forward and backward
         q3, k3, v3, do3 = (x.reshape(BH, N, d) for x in (q, kk, v, do))
         od = torch.empty((BH, N, d), dtype=torch.float32, device=dev)
