@@ -414,11 +414,13 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void
 #define LH_G4(D, LM) k_scatter_g4<D, LM><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype)
     if (s.d == 128) {
       if (s.L <= 3) LH_G4(128, 3);
-      else if (s.L <= 5) LH_G4(128, 5);
+      else if (s.L == 4) LH_G4(128, 4);
+      else if (s.L == 5) LH_G4(128, 5);
       else LH_G4(128, kMaxL);
     } else {
       if (s.L <= 3) LH_G4(64, 3);
-      else if (s.L <= 5) LH_G4(64, 5);
+      else if (s.L == 4) LH_G4(64, 4);
+      else if (s.L == 5) LH_G4(64, 5);
       else LH_G4(64, kMaxL);
     }
 #undef LH_G4
@@ -457,11 +459,13 @@ hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, co
 #define LH_PB(D, LM) k_pool_bwd_g4<D, LM><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype)
     if (s.d == 128) {
       if (s.L <= 3) LH_PB(128, 3);
-      else if (s.L <= 5) LH_PB(128, 5);
+      else if (s.L == 4) LH_PB(128, 4);
+      else if (s.L == 5) LH_PB(128, 5);
       else LH_PB(128, kMaxL);
     } else {
       if (s.L <= 3) LH_PB(64, 3);
-      else if (s.L <= 5) LH_PB(64, 5);
+      else if (s.L == 4) LH_PB(64, 4);
+      else if (s.L == 5) LH_PB(64, 5);
       else LH_PB(64, kMaxL);
     }
 #undef LH_PB
