@@ -66,8 +66,9 @@ ATTN_STAGES = {
 def hbm_stage_bytes(cfg: dict, S: int) -> dict:
     """Algorithmic HBM bytes of the memory-bound stages for one step: what each
     stage must read and write once (bf16 or fp32 storage of Q, K, V, O and the
-    gradients as the workload has it; O~, dQ~, dK~, dV~ in fp32; scores fp32;
-    keys 8 bytes; flags 1 byte; slot map and coordinates 4 bytes)."""
+    gradients as the workload has it; O~, dQ~, dK~, dV~ in fp32; scores fp32,
+    read by the top-k's histogram and filter passes; flags 1 byte; slot map and
+    coordinates 4 bytes)."""
     B, H, N, d, L, p = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["L"], cfg["p"]
     BH = B * H
     io = 2 if cfg["dtype"] == "bf16" else 4
@@ -76,8 +77,8 @@ def hbm_stage_bytes(cfg: dict, S: int) -> dict:
     Sv = (S + 63) // 64 * 64
     r16, r32 = d * io, d * 4
     return {
-        "pool_score": BH * (3 * N * r16 + 3 * sum(n[1:]) * r16 + 2 * P * 4 + E * 8),
-        "topk": BH * (2 * E * 8 + P),
+        "pool_score": BH * (3 * N * r16 + 3 * sum(n[1:]) * r16 + 2 * P * 4),
+        "topk": BH * (2 * E * 2 * 4 + P),
         "gather": BH * (2 * P + P * 4 + S * 4 + 2 * 3 * S * r16),
         "scatter": BH * (S * r32 + P * 4 + N * r16),
         "scatter_bwd": BH * (N * r16 + S * r32 + 2 * S * 4 + Sv * r16 + Sv * 8),

@@ -6,22 +6,18 @@
 //   Sec. 3.4  level-0 scores are the per-head l2 norms ||Q_t|| (query score QK)
 //             and ||K_t|| (key score KQ); coarser levels take the max of the
 //             level-0 scores over their window.
-// For every candidate entry (levels 0..L-2) the kernel also writes the 64-bit
-// selection key used by the top-k:
-//   key = bits(max(QK, KQ)) << 32 | (0xFFFFFFFF - g),
-// g = f if QK >= KQ else P + f (stream index of the larger score; f = flat
-// index).  Scores are non-negative, so the float bits order like the values,
-// and "larger key" means "larger score, then lower stream index": the order of
-// the joint selection over the concatenated QK || KQ stream.
+// It also records, per head, the range of the candidates' score bits (levels
+// 0..L-2, both streams) for the top-k histogram.
 //
-// Work mapping: a work-group of 256 threads covers RG row-groups x CH column
-// chunks of EL elements (EL = 8 up to three levels, 4 beyond, which halves the
-// per-level accumulators so that more wavefronts fit).  Row-group rg owns one
-// coarsest window of G = p^(L-1) consecutive rows and walks it top to bottom,
-// reading each row one step ahead of its use, so every pooled window and every
-// max-pool lives in one thread's registers; only the norm of a row needs a
-// reduction, across the CH lanes that hold it (adjacent lanes of one
-// wavefront, reduced with xor shuffles).
+// Work mapping: grid plane z = 0, 1, 2 pools Q, K, V respectively; the Q and K
+// planes also compute the query and key scores.  A work-group of 256 threads
+// covers RG row-groups x CH column chunks of EL elements (EL = 8 up to four
+// levels, 4 beyond, which halves the per-level accumulators so that more
+// wavefronts fit).  Row-group rg owns one coarsest window of G = p^(L-1)
+// consecutive rows and walks it top to bottom, reading each row one step ahead
+// of its use, so every pooled window and every max-pool lives in one thread's
+// registers; only the norm of a row needs a reduction, across the CH lanes that
+// hold it (adjacent lanes of one wavefront, reduced with xor shuffles).
 #include "lh_internal.h"
 
 namespace lh {
@@ -87,104 +83,69 @@ template <typename T, int N> struct VecN;
 template <typename T> struct VecN<T, 4> : Vec4<T> {};
 template <typename T> struct VecN<T, 8> : Vec8<T> {};
 
-__device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f, int P) {
-  const float r = fmaxf(qk, kq);
-  const unsigned int g = (qk >= kq) ? (unsigned int)f : (unsigned int)(P + f);
-  return ((unsigned long long)__float_as_uint(r) << 32) | (unsigned long long)(0xFFFFFFFFu - g);
-}
 
 template <typename T, int D, int ML>
 __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v, char *__restrict__ ws, FwdWs w,
                                                     float *__restrict__ scores) {
-  constexpr int EL = ML <= 3 ? 8 : 4;   // elements per lane
-  constexpr int CH = D / EL;         // threads per row
-  constexpr int RG = 256 / CH;       // row-groups per work-group
+  constexpr int EL = ML <= 4 ? 8 : 4;   // elements per lane
+  constexpr int CH = D / EL;            // threads per row
+  constexpr int RG = 256 / CH;          // row-groups per work-group
   const int h = blockIdx.y;
+  const int z = blockIdx.z;             // 0: Q and its scores, 1: K and its scores, 2: V
+  const bool scored = z < 2;
   const int j = threadIdx.x % CH;
   const int rg = threadIdx.x / CH;
   const int L = s.L;
   const int G = s.pw[L - 1];
   const long long win = (long long)blockIdx.x * RG + rg;   // coarsest window index
   const bool active = win < s.n[L - 1];
-  const int P = s.P;
-
+  const T *x = z == 0 ? q : (z == 1 ? k : v);
   const long long hoff = (long long)h * s.N * D;
-  float *sc_qk = scores + (long long)h * 2 * P;
-  float *sc_kq = sc_qk + P;
-  unsigned long long *keys = reinterpret_cast<unsigned long long *>(ws + w.keys) + (long long)h * s.E;
+  float *sc = scores + (long long)h * 2 * s.P + (z == 1 ? s.P : 0);   // QK or KQ stream
 
   // running window sums and max-pooled scores per level l >= 1 (ML >= L levels)
-  float aq[ML][EL], ak[ML][EL], av[ML][EL];
-  float ma[ML], mb[ML];
+  float acc[ML][EL], mx[ML];
 #pragma unroll
   for (int l = 0; l < ML; ++l) {
-    ma[l] = 0.f;
-    mb[l] = 0.f;
+    mx[l] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
+    for (int e = 0; e < EL; ++e) acc[l][e] = 0.f;
   }
   unsigned int umin = 0xFFFFFFFFu, umax = 0u;
 
   const long long t0 = win * G;
   // the rows of the window are read one ahead of their use
   const long long last = active ? t0 + G - 1 : 0;
-  float nq[EL], nk[EL], nv[EL];
-  {
-    const long long t = active ? t0 : 0;
-    VecN<T, EL>::load(q + hoff + t * D + j * EL, nq);
-    VecN<T, EL>::load(k + hoff + t * D + j * EL, nk);
-    VecN<T, EL>::load(v + hoff + t * D + j * EL, nv);
-  }
+  float nx[EL];
+  VecN<T, EL>::load(x + hoff + (active ? t0 : 0) * D + j * EL, nx);
   for (int r = 0; r < G; ++r) {
     const long long t = t0 + r;
-    float xq[EL], xk[EL], xv[EL];
+    float xr[EL];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      xq[e] = active ? nq[e] : 0.f;
-      xk[e] = active ? nk[e] : 0.f;
-      xv[e] = active ? nv[e] : 0.f;
-    }
-    {
-      const long long tn = active ? min(t + 1, last) : 0;
-      VecN<T, EL>::load(q + hoff + tn * D + j * EL, nq);
-      VecN<T, EL>::load(k + hoff + tn * D + j * EL, nk);
-      VecN<T, EL>::load(v + hoff + tn * D + j * EL, nv);
-    }
-    float sq = 0.f, sk = 0.f;
+    for (int e = 0; e < EL; ++e) xr[e] = active ? nx[e] : 0.f;
+    VecN<T, EL>::load(x + hoff + (active ? min(t + 1, last) : 0) * D + j * EL, nx);
+    float a = 0.f;
+    if (scored) {
+      float sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      sq = fmaf(xq[e], xq[e], sq);
-      sk = fmaf(xk[e], xk[e], sk);
-    }
+      for (int e = 0; e < EL; ++e) sq = fmaf(xr[e], xr[e], sq);
 #pragma unroll
-    for (int m = 1; m < CH; m <<= 1) {
-      sq += __shfl_xor(sq, m, CH);
-      sk += __shfl_xor(sk, m, CH);
-    }
-    const float a = sqrtf(sq);
-    const float b = sqrtf(sk);
-    if (active && j == 0) {
-      sc_qk[t] = a;
-      sc_kq[t] = b;
-      if (L > 1) {
-        const unsigned long long key = make_key(a, b, (int)t, P);
-        keys[t] = key;
-        const unsigned int hi = (unsigned int)(key >> 32);
-        umin = min(umin, hi);
-        umax = max(umax, hi);
+      for (int m = 1; m < CH; m <<= 1) sq += __shfl_xor(sq, m, CH);
+      a = sqrtf(sq);
+      if (active && j == 0) {
+        sc[t] = a;
+        if (L > 1) {
+          umin = min(umin, __float_as_uint(a));
+          umax = max(umax, __float_as_uint(a));
+        }
       }
     }
     if (L == 1) continue;
     // level 1 accumulates rows; level l+1 accumulates completed level-l windows
 #pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      aq[1][e] += xq[e];
-      ak[1][e] += xk[e];
-      av[1][e] += xv[e];
-    }
-    ma[1] = fmaxf(ma[1], a);
-    mb[1] = fmaxf(mb[1], b);
+    for (int e = 0; e < EL; ++e) acc[1][e] += xr[e];
+    mx[1] = fmaxf(mx[1], a);
 #pragma unroll
     for (int l = 1; l < ML; ++l) {
       if (l >= L) break;
@@ -192,48 +153,32 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
       const long long i = (t + 1) / s.pw[l] - 1;
       const float inv = 1.0f / (float)s.pw[l];
       if (active) {
-        float mq[EL], mk[EL], mv[EL];
+        float mean[EL];
 #pragma unroll
-        for (int e = 0; e < EL; ++e) {
-          mq[e] = aq[l][e] * inv;
-          mk[e] = ak[l][e] * inv;
-          mv[e] = av[l][e] * inv;
-        }
-        const long long lo = ((long long)h * s.n[l] + i) * D + j * EL;
-        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][0]) + lo, mq);
-        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][1]) + lo, mk);
-        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][2]) + lo, mv);
-        if (j == 0) {
-          const int f = s.off[l] + (int)i;
-          sc_qk[f] = ma[l];
-          sc_kq[f] = mb[l];
+        for (int e = 0; e < EL; ++e) mean[e] = acc[l][e] * inv;
+        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][z]) + ((long long)h * s.n[l] + i) * D + j * EL, mean);
+        if (scored && j == 0) {
+          sc[s.off[l] + (int)i] = mx[l];
           if (l <= L - 2) {
-            const unsigned long long key = make_key(ma[l], mb[l], f, P);
-            keys[f] = key;
-            const unsigned int hi = (unsigned int)(key >> 32);
-            umin = min(umin, hi);
-            umax = max(umax, hi);
+            umin = min(umin, __float_as_uint(mx[l]));
+            umax = max(umax, __float_as_uint(mx[l]));
           }
         }
       }
       if (l + 1 < ML && l + 1 < L) {
 #pragma unroll
-        for (int e = 0; e < EL; ++e) {
-          aq[l + 1][e] += aq[l][e];
-          ak[l + 1][e] += ak[l][e];
-          av[l + 1][e] += av[l][e];
-        }
-        ma[l + 1] = fmaxf(ma[l + 1], ma[l]);
-        mb[l + 1] = fmaxf(mb[l + 1], mb[l]);
+        for (int e = 0; e < EL; ++e) acc[l + 1][e] += acc[l][e];
+        mx[l + 1] = fmaxf(mx[l + 1], mx[l]);
       }
 #pragma unroll
-      for (int e = 0; e < EL; ++e) aq[l][e] = ak[l][e] = av[l][e] = 0.f;
-      ma[l] = 0.f;
-      mb[l] = 0.f;
+      for (int e = 0; e < EL; ++e) acc[l][e] = 0.f;
+      mx[l] = 0.f;
     }
   }
-  if (L == 1) return;
-  // score-bit range of the candidates, for the top-k histogram
+  if (L == 1 || !scored) return;
+  // range of the candidates' score bits over both streams (a key's upper half is
+  // the larger of its two scores, so this range contains every key's), for the
+  // top-k histogram
   __shared__ unsigned int red_min[256], red_max[256];
   red_min[threadIdx.x] = umin;
   red_max[threadIdx.x] = umax;
@@ -284,10 +229,10 @@ static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                              const FwdWs &w, float *scores, hipStream_t st) {
   if (s.L > kMaxL) return hipErrorInvalidValue;
-  const int CH = s.d / (s.L <= 3 ? 8 : 4);   // elements per lane as in the kernel (ML <= 3: 8)
+  const int CH = s.d / (s.L <= 4 ? 8 : 4);   // elements per lane as in the kernel (ML <= 3: 8)
   const int RG = 256 / CH;
   const int nwin = s.n[s.L - 1];
-  dim3 grid((nwin + RG - 1) / RG, s.BH);
+  dim3 grid((nwin + RG - 1) / RG, s.BH, 3);   // one plane per tensor: Q, K, V
   char *wsb = reinterpret_cast<char *>(ws);
   if (s.io == LH_BF16) {
     if (s.d == 128) pool_score_ml<uint16_t, 128>(s, grid, q, k, v, wsb, w, scores, st);

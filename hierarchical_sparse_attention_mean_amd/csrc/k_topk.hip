@@ -3,17 +3,18 @@
 // "Long Context Pre-Training with Lighthouse Attention", Sec. 3.4: selection
 // runs jointly over the concatenated QK and KQ streams across levels; the
 // coarsest level is always kept; Sec. 3.5: the non-coarsest levels contribute
-// B = (L-1) p k entries (here min(B, |E|), distinct entries).  The keys written
-// by the pool/score kernel are unique and order entries by (score desc, stream
-// index asc), so the selection is exactly "the B largest keys".
+// B = (L-1) p k entries (here min(B, |E|), distinct entries).  The 64-bit key of
+// a candidate, formed from its two scores (make_key), is unique and orders the
+// entries by (score desc, stream index asc), so the selection is exactly "the B
+// largest keys".
 //
 // The paper's kernel keeps a per-chunk top-m buffer by bitonic merging.  Here
 // the same exact set is found in a bounded number of passes that do not depend
 // on k:
-//   1. k_topk_hist    one pass over the keys: LDS histogram of a 12-bit digit of
+//   1. k_topk_hist    one pass over the scores: LDS histogram of a 12-bit digit of
 //                     the score bits, rescaled to the per-head [min, max] range
 //                     that the score kernel recorded; merged with global atomics.
-//   2. k_topk_filter  one pass over the keys: every work-group finds the boundary
+//   2. k_topk_filter  one pass over the scores: every work-group finds the boundary
 //                     bin from the histogram; keys above it are flagged, keys in
 //                     it are appended to a per-head candidate list.
 //   3. k_topk_refine  one work-group per head takes the `need` largest of the
@@ -47,16 +48,17 @@ __device__ __forceinline__ int key_flat(unsigned long long key, int P) {
   return (int)(g >= (unsigned int)P ? g - (unsigned int)P : g);
 }
 
-__global__ __launch_bounds__(256) void k_topk_hist(Shape s, char *__restrict__ ws, FwdWs w) {
+__global__ __launch_bounds__(256) void k_topk_hist(Shape s, char *__restrict__ ws, FwdWs w,
+                                                   const float *__restrict__ scores) {
   __shared__ unsigned int hist[kHistBins];
   const int h = blockIdx.y;
   for (int i = threadIdx.x; i < kHistBins; i += 256) hist[i] = 0;
   const TopkState st = reinterpret_cast<const TopkState *>(ws + w.state)[h];
   const int sh = digit_shift(st.umin, st.umax);
   __syncthreads();
-  const unsigned long long *keys = reinterpret_cast<const unsigned long long *>(ws + w.keys) + (long long)h * s.E;
+  const float *qk = scores + (long long)h * 2 * s.P, *kq = qk + s.P;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < s.E; i += (long long)gridDim.x * 256)
-    atomicAdd(&hist[key_digit(keys[i], st.umin, sh)], 1u);
+    atomicAdd(&hist[key_digit(make_key(qk[i], kq[i], (int)i, s.P), st.umin, sh)], 1u);
   __syncthreads();
   unsigned int *gh = reinterpret_cast<unsigned int *>(ws + w.hist) + (long long)h * kHistBins;
   for (int i = threadIdx.x; i < kHistBins; i += 256)
@@ -110,7 +112,7 @@ __device__ int find_boundary(const unsigned int *gh, long long Bsel, long long *
 }
 
 __global__ __launch_bounds__(256) void k_topk_filter(Shape s, char *__restrict__ ws, FwdWs w,
-                                                     uint8_t *__restrict__ flags) {
+                                                     const float *__restrict__ scores, uint8_t *__restrict__ flags) {
   const int h = blockIdx.y;
   TopkState *stp = reinterpret_cast<TopkState *>(ws + w.state) + h;
   const TopkState st = *stp;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(Shape s, char *__restrict__
     stp->need = (bstar < 0 || bstar >= kHistBins) ? 0 : (long long)s.Bsel - above;
   }
   const int sh = digit_shift(st.umin, st.umax);
-  const unsigned long long *keys = reinterpret_cast<const unsigned long long *>(ws + w.keys) + (long long)h * s.E;
+  const float *qk = scores + (long long)h * 2 * s.P, *kq = qk + s.P;
   unsigned long long *cand = reinterpret_cast<unsigned long long *>(ws + w.cand) + (long long)h * s.E;
   uint8_t *fl = flags + (long long)h * s.P;
   const int lane = threadIdx.x & 63;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void k_topk_filter(Shape s, char *__restrict__
     bool boundary = false;
     unsigned long long key = 0;
     if (i < s.E) {
-      key = keys[i];
+      key = make_key(qk[i], kq[i], (int)i, s.P);
       const int dg = (bstar < 0) ? kHistBins : (bstar >= kHistBins ? -1 : key_digit(key, st.umin, sh));
       fl[i] = (uint8_t)(dg > bstar ? 1 : 0);
       boundary = (dg == bstar);
@@ -321,15 +323,16 @@ hipError_t launch_topk_init(const Shape &s, void *ws, const FwdWs &w, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, uint8_t *flags, hipStream_t st) {
+hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, const float *scores, uint8_t *flags,
+                       hipStream_t st) {
   char *wsb = reinterpret_cast<char *>(ws);
   const bool partial = s.Bsel > 0 && s.Bsel < s.E;
   if (partial) {
     const int nb = (int)((s.E + 256 * 16 - 1) / (256 * 16));
-    k_topk_hist<<<dim3(nb, s.BH), 256, 0, st>>>(s, wsb, w);
+    k_topk_hist<<<dim3(nb, s.BH), 256, 0, st>>>(s, wsb, w, scores);
   }
   const int nbf = (int)((s.P + 256 * 8 - 1) / (256 * 8));
-  k_topk_filter<<<dim3(nbf, s.BH), 256, 0, st>>>(s, wsb, w, flags);
+  k_topk_filter<<<dim3(nbf, s.BH), 256, 0, st>>>(s, wsb, w, scores, flags);
   if (partial) k_topk_refine<<<dim3(s.BH), kRefineThreads, 0, st>>>(s, wsb, w, flags);
   return hipGetLastError();
 }

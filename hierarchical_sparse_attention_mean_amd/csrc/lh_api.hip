@@ -190,7 +190,6 @@ void fwd_ws_layout(const lh::Shape &s, lh::FwdWs *w) {
   memset(w, 0, sizeof *w);
   for (int l = 1; l < s.L; ++l)
     for (int t = 0; t < 3; ++t) w->lev[l][t] = take(es * BH * (size_t)s.n[l] * d);
-  w->keys = take(8 * BH * (size_t)s.E);
   // state and histogram are adjacent: one fill kernel clears both
   w->state = take(sizeof(lh::TopkState) * BH);
   w->hist = cur;
@@ -446,7 +445,7 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   // (ii) selection
   {
     Span sp(LH_STAGE_TOPK, hs);
-    if ((st = hip_check(lh::launch_topk(s, ws, fw, flags, hs), "topk")) != LH_OK) return st;
+    if ((st = hip_check(lh::launch_topk(s, ws, fw, scores, flags, hs), "topk")) != LH_OK) return st;
   }
   // (iii) topological compaction + gather
   {

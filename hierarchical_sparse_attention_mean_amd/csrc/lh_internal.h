@@ -49,7 +49,6 @@ struct TopkState {
 // Forward workspace layout (byte offsets).
 struct FwdWs {
   size_t lev[LH_MAX_LEVELS][3];  // pooled Q, K, V of level l >= 1 ([BH][n_l][d], io dtype)
-  size_t keys;                   // uint64 [BH][E]
   size_t state;                  // TopkState [BH]
   size_t hist;                   // uint32 [BH][kHistBins]
   size_t cand;                   // uint64 [BH][E]
@@ -111,12 +110,25 @@ template <> struct IO<uint16_t> {
   static __device__ __forceinline__ void st(uint16_t *p, long long i, float v) { p[i] = f32_to_bf16_rne(v); }
 };
 
+// 64-bit selection key of candidate f (flat index) from its two scores:
+//   key = bits(max(QK, KQ)) << 32 | (0xFFFFFFFF - g),
+// g = f if QK >= KQ else P + f (stream index of the larger score).  Scores are
+// non-negative, so the float bits order like the values, and "larger key"
+// means "larger score, then lower stream index": the order of the joint
+// selection over the concatenated QK || KQ stream.  Keys are unique.
+__device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f, int P) {
+  const float r = fmaxf(qk, kq);
+  const unsigned int g = (qk >= kq) ? (unsigned int)f : (unsigned int)(P + f);
+  return ((unsigned long long)__float_as_uint(r) << 32) | (unsigned long long)(0xFFFFFFFFu - g);
+}
+
 // ---- launchers (each enqueues on `st`, returns hipGetLastError()) ----
 hipError_t launch_fill_u32(void *p, size_t n_u32, unsigned int value, hipStream_t st);
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                              const FwdWs &w, float *scores, hipStream_t st);
 hipError_t launch_topk_init(const Shape &s, void *ws, const FwdWs &w, hipStream_t st);
-hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, uint8_t *flags, hipStream_t st);
+hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, const float *scores, uint8_t *flags,
+                       hipStream_t st);
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                                  const FwdWs &w, const uint8_t *flags, int *slot, int *coords,
                                  void *qt, void *kt, void *vt, hipStream_t st);
