@@ -166,6 +166,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 st = (f32x16){}, dp = (f32x16){};
+      // the wavefronts of a SIMD alternate between runs of products and the dS
+      // arithmetic; a run of products is issued at raised priority so that the
+      // matrix core is kept fed while the other wavefront computes
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const int j = kb * NH + 2 * c;
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(win[(j + 1) % kDqWin], gf[c], dp, 0, 0, 0);
         next(j + 1);
       }
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -184,6 +189,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
         }
         dsf[i >> 3][i & 7] = (__bf16)(pj * (dp[i] - dl));
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int r = 0; r < 2 * DB; ++r) {   // dQ~^T += K~^T dS^T over the half's two 16-key chunks
         const int j = kb * NH + NA + r;
@@ -191,6 +197,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(int S, int Sv, in
         next(j);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     static_assert(kDqWin <= NA, "the reads kept in flight are single reads");
     tiles::wait_fills_barrier_keep<kFillOps, kDqWin>();   // tile t+2 landed; the window's reads (tile t+1) stay in flight
   };
