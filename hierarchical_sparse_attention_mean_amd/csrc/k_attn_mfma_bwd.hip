@@ -361,16 +361,23 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
       f[c] = tiles::tr_frag(tile + 16 * cc * T::WR, otr[b][0], otr[b][1]);
     }
   };
+  // The P wavefront's runs of products are issued at raised wave priority (its
+  // P feeds the dS wavefront one tile later); measured 3-4% faster than equal
+  // priorities, while raising the dS wavefront's instead was slower.
   auto rowmm = [&](const bf16x8 (&f)[KC]) {
     f32x16 r = (f32x16){};
+    if (!dsw) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < KC; ++c) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], kv[c], r, 0, 0, 0);
+    if (!dsw) __builtin_amdgcn_s_setprio(0);
     return r;
   };
   auto colmm = [&](const bf16x8 (&f)[KC], const bf16x8 *x) {
+    if (!dsw) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       acc[c % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[c], x[c / DB], acc[c % DB], 0, 0, 0);
+    if (!dsw) __builtin_amdgcn_s_setprio(0);
   };
 
   if (!dsw) {
