@@ -13,6 +13,10 @@
 // i = floor((t+1) / p^l) - 1, so each output element pulls its <= L
 // contributions and owns its accumulator.
 //
+// When p is a power of two >= 4 the scatter runs in two passes (coarser levels
+// for every position, then the few positions with a selected level-0 entry);
+// see k_scatter_hi / k_scatter_lo.
+//
 // Adjoints (Sec. 3.2: gradients flow through scatter, attention, gather and
 // pool; the selection is frozen):
 //   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m;
@@ -117,87 +121,130 @@ __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict_
   store_row8(o, o_dtype, ((long long)h * s.N + (u - 1)) * D + c * 8, q);
 }
 
-// p a power of two, p >= 4 (so every p^l with l >= 1 is a multiple of 4).  One
-// thread per (group of 4 positions, 8-element chunk): the group's positions
-// u = u0 .. u0 + 3 (u = t + 1, u0 a multiple of 4) share their entry of every
-// level l >= 1 (i = (u0 >> l log2 p) - 1) and have one level-0 entry each.  All
-// slots are looked up first, then all rows are loaded (one row per level >= 1
-// and four of level 0), so each thread has two dependent memory round trips
-// for four output rows.
+constexpr int kScatterGroups = 2;   // groups of 4 positions per thread in k_scatter_hi
+
+// p a power of two, p >= 4 (so every p^l with l >= 1 is a multiple of 4), in
+// two passes.
+//   k_scatter_hi   one thread per (NG groups of 4 positions, 8-element chunk):
+//                  the positions u = u0 .. u0 + 3 (u = t + 1, u0 a multiple of
+//                  4) share their entry of every level l >= 1 (i = (u0 >> l
+//                  log2 p) - 1), so a group needs one slot lookup and one row
+//                  per coarser level.  All lookups of the thread's groups are
+//                  issued first, then all rows.  Writes every position's sum
+//                  over its coarser levels.
+//   k_scatter_lo   one thread per (gathered row, 8-element chunk); rows of
+//                  level 0 (a few percent of them) rewrite their position's
+//                  output with the full sum, their own row included.
+// Both form the same fixed-point sum, so the result does not depend on which
+// pass wrote a position last.
+template <int LM>
+__device__ __forceinline__ void fixed_out(const float (&xs)[LM][8], const bool (&has)[LM], float (&q)[8]) {
+  bool big = false;
+  double a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = 0.0;
+#pragma unroll
+  for (int l = 0; l < LM; ++l) {
+    if (!has[l]) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      big |= !(fabsf(xs[l][e]) < 262144.f);
+      a[e] += (double)rintf(xs[l][e] * 4294967296.0f);
+    }
+  }
+  if (!big) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = (float)(a[e] * 2.3283064365386963e-10);
+  } else {
+    for (int e = 0; e < 8; ++e) {
+      long long b = 0;
+      for (int l = 0; l < LM; ++l)
+        if (has[l]) b += to_fixed(xs[l][e]);
+      q[e] = from_fixed(b);
+    }
+  }
+}
+
 template <int D, int LM>
-__global__ __launch_bounds__(256) void k_scatter_g4(Shape s, const int *__restrict__ slot,
+__global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restrict__ slot,
                                                     const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
   constexpr int C8 = D / 8;
+  constexpr int NG = kScatterGroups;
+  constexpr int GPP = 256 / C8;   // groups per pass of the work-group
   const int h = blockIdx.y;
   const int c = threadIdx.x % C8;
-  const int u0 = 4 * (blockIdx.x * (256 / C8) + threadIdx.x / C8);
-  if (u0 > s.N) return;
   const int lg = __builtin_ctz(s.p);
   const int *sl = slot + (long long)h * s.P;
   const float *ob = ot + (long long)h * s.S * D + c * 8;
-  int m0[4], mh[LM];
+  int u0[NG], mh[NG][LM];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int u = u0 + r;
-    m0[r] = (u >= 1 && u <= s.N) ? sl[u - 1] : -1;
+  for (int g = 0; g < NG; ++g) {
+    u0[g] = 4 * (blockIdx.x * (GPP * NG) + g * GPP + threadIdx.x / C8);
+#pragma unroll
+    for (int l = 0; l < LM; ++l) {
+      mh[g][l] = -1;
+      if (l >= 1 && l < s.L && u0[g] <= s.N) {
+        const int i = (u0[g] >> (l * lg)) - 1;
+        if (i >= 0) mh[g][l] = sl[s.off[l] + i];
+      }
+    }
   }
+  float xs[NG][LM][8];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int l = 1; l < LM; ++l)
+      if (mh[g][l] >= 0) load_row8(ob + (long long)mh[g][l] * D, xs[g][l]);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    bool has[LM];
+#pragma unroll
+    for (int l = 0; l < LM; ++l) has[l] = l >= 1 && mh[g][l] >= 0;
+    float q[8];
+    fixed_out<LM>(xs[g], has, q);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = u0[g] + r - 1;
+      if (t >= 0 && t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
+    }
+  }
+}
+
+template <int D, int LM>
+__global__ __launch_bounds__(256) void k_scatter_lo(Shape s, const int *__restrict__ slot,
+                                                    const int *__restrict__ coords, const float *__restrict__ ot,
+                                                    void *__restrict__ o, int o_dtype) {
+  constexpr int C8 = D / 8;
+  const int h = blockIdx.y;
+  const int c = threadIdx.x % C8;
+  const int m = blockIdx.x * (256 / C8) + threadIdx.x / C8;
+  if (m >= s.S) return;
+  const int t = coords[(long long)h * s.S + m];
+  if (t >= s.N) return;   // not a level-0 entry (flat indices of level 0 are 0 .. N-1)
+  const int lg = __builtin_ctz(s.p);
+  const int u = t + 1;
+  const int *sl = slot + (long long)h * s.P;
+  const float *ob = ot + (long long)h * s.S * D + c * 8;
+  int mh[LM];
+  mh[0] = m;
 #pragma unroll
   for (int l = 1; l < LM; ++l) {
     mh[l] = -1;
     if (l < s.L) {
-      const int i = (u0 >> (l * lg)) - 1;
+      const int i = (u >> (l * lg)) - 1;
       if (i >= 0) mh[l] = sl[s.off[l] + i];
     }
   }
-  float xh[LM][8], x0[4][8];
+  float xs[LM][8];
+  bool has[LM];
 #pragma unroll
-  for (int l = 1; l < LM; ++l)
-    if (mh[l] >= 0) load_row8(ob + (long long)mh[l] * D, xh[l]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (m0[r] >= 0) load_row8(ob + (long long)m0[r] * D, x0[r]);
-  bool big = false;
-  double hs[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hs[e] = 0.0;
-#pragma unroll
-  for (int l = 1; l < LM; ++l) {
-    if (mh[l] < 0) continue;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      big |= !(fabsf(xh[l][e]) < 262144.f);
-      hs[e] += (double)rintf(xh[l][e] * 4294967296.0f);
-    }
+  for (int l = 0; l < LM; ++l) {
+    has[l] = mh[l] >= 0;
+    if (has[l]) load_row8(ob + (long long)mh[l] * D, xs[l]);
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (m0[r] < 0) continue;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) big |= !(fabsf(x0[r][e]) < 262144.f);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = u0 + r - 1;
-    if (t < 0 || t >= s.N) continue;
-    float q[8];
-    if (!big) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double a = m0[r] >= 0 ? hs[e] + (double)rintf(x0[r][e] * 4294967296.0f) : hs[e];
-        q[e] = (float)(a * 2.3283064365386963e-10);
-      }
-    } else {
-      long long b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int l = 1; l < LM; ++l) {
-        if (mh[l] < 0) continue;
-        for (int e = 0; e < 8; ++e) b[e] += to_fixed(ob[(long long)mh[l] * D + e]);
-      }
-      if (m0[r] >= 0)
-        for (int e = 0; e < 8; ++e) b[e] += to_fixed(ob[(long long)m0[r] * D + e]);
-      for (int e = 0; e < 8; ++e) q[e] = from_fixed(b[e]);
-    }
-    store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
-  }
+  float q[8];
+  fixed_out<LM>(xs, has, q);
+  store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
 }
 
 // One thread per (slot m, 8-column chunk): 256 / (D / 8) slots per work-group.
@@ -407,23 +454,30 @@ __global__ __launch_bounds__(256) void k_pool_bwd_g4(Shape s, const int *__restr
 
 }  // namespace
 
-hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void *o, int o_dtype, hipStream_t st) {
-  const int per = 256 / (s.d / 8);   // positions (or groups of 4 positions) per work-group
+hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, const float *ot, void *o,
+                          int o_dtype, hipStream_t st) {
+  const int per = 256 / (s.d / 8);   // positions (or groups of 4 positions) per pass of a work-group
   if (s.p >= 4 && (s.p & (s.p - 1)) == 0) {
-    dim3 grid((unsigned)((s.N / 4 + 1 + per - 1) / per), s.BH);   // groups u0 = 0, 4, ..., <= N
-#define LH_G4(D, LM) k_scatter_g4<D, LM><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype)
+    const int gpb = per * kScatterGroups;
+    dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // groups u0 = 0, 4, ..., <= N
+    dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);
+#define LH_SC(D, LM)                                                                                 \
+  do {                                                                                               \
+    k_scatter_hi<D, LM><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);                             \
+    k_scatter_lo<D, LM><<<glo, 256, 0, st>>>(s, slot, coords, ot, o, o_dtype);                      \
+  } while (0)
     if (s.d == 128) {
-      if (s.L <= 3) LH_G4(128, 3);
-      else if (s.L == 4) LH_G4(128, 4);
-      else if (s.L == 5) LH_G4(128, 5);
-      else LH_G4(128, kMaxL);
+      if (s.L <= 3) LH_SC(128, 3);
+      else if (s.L == 4) LH_SC(128, 4);
+      else if (s.L == 5) LH_SC(128, 5);
+      else LH_SC(128, kMaxL);
     } else {
-      if (s.L <= 3) LH_G4(64, 3);
-      else if (s.L == 4) LH_G4(64, 4);
-      else if (s.L == 5) LH_G4(64, 5);
-      else LH_G4(64, kMaxL);
+      if (s.L <= 3) LH_SC(64, 3);
+      else if (s.L == 4) LH_SC(64, 4);
+      else if (s.L == 5) LH_SC(64, 5);
+      else LH_SC(64, kMaxL);
     }
-#undef LH_G4
+#undef LH_SC
   } else {
     dim3 grid((unsigned)((s.N + 1 + per - 1) / per), s.BH);       // u = 0 .. N
     if (s.d == 128) k_scatter<128><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);

@@ -468,7 +468,7 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   // (iv) scatter-back
   {
     Span sp(LH_STAGE_SCATTER, hs);
-    if ((st = hip_check(lh::launch_scatter(s, slot, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
+    if ((st = hip_check(lh::launch_scatter(s, slot, coords, ot, o, o_dtype, hs), "scatter")) != LH_OK) return st;
   }
   return LH_OK;
 }

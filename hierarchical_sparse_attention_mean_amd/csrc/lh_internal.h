@@ -132,8 +132,8 @@ hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, const float *sc
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                                  const FwdWs &w, const uint8_t *flags, int *slot, int *coords,
                                  void *qt, void *kt, void *vt, hipStream_t st);
-hipError_t launch_scatter(const Shape &s, const int *slot, const float *ot, void *o, int o_dtype,
-                          hipStream_t st);
+hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, const float *ot, void *o,
+                          int o_dtype, hipStream_t st);
 hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
                               const float *lse, float *dot32, uint16_t *dotb, float *delta, float *rows,
                               hipStream_t st);
