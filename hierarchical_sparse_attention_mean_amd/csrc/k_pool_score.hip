@@ -14,9 +14,9 @@
 // covers RG row-groups x CH column chunks of EL elements (EL = 8 up to four
 // levels, 4 beyond, which halves the per-level accumulators so that more
 // wavefronts fit).  Row-group rg owns one coarsest window of G = p^(L-1)
-// consecutive rows and walks it top to bottom, reading each row one step ahead
-// of its use, so every pooled window and every max-pool lives in one thread's
-// registers; only the norm of a row needs a reduction, across the CH lanes that
+// consecutive rows and walks it top to bottom, reading its rows in batches
+// (2 rows up to three levels, 8 beyond) one batch ahead of their use, so
+// every pooled window and every max-pool lives in one thread's registers; only the norm of a row needs a reduction, across the CH lanes that
 // hold it (adjacent lanes of one wavefront, reduced with xor shuffles).
 #include "lh_internal.h"
 
@@ -37,11 +37,6 @@ template <> struct Vec4<float> {
   }
 };
 template <> struct Vec4<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t *p, float (&x)[4]) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(p);
-    x[0] = __uint_as_float(a.x << 16); x[1] = __uint_as_float(a.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(a.y << 16); x[3] = __uint_as_float(a.y & 0xFFFF0000u);
-  }
   static __device__ __forceinline__ void store(uint16_t *p, const float (&x)[4]) {
     *reinterpret_cast<uint2 *>(p) = make_uint2((unsigned)f32_to_bf16_rne(x[0]) | ((unsigned)f32_to_bf16_rne(x[1]) << 16),
                                                (unsigned)f32_to_bf16_rne(x[2]) | ((unsigned)f32_to_bf16_rne(x[3]) << 16));
@@ -61,15 +56,6 @@ template <> struct Vec8<float> {
   }
 };
 template <> struct Vec8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t *p, float (&x)[8]) {
-    const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
-    const unsigned int w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
   static __device__ __forceinline__ void store(uint16_t *p, const float (&x)[8]) {
     unsigned int w[4];
 #pragma unroll
@@ -84,6 +70,38 @@ template <typename T> struct VecN<T, 4> : Vec4<T> {};
 template <typename T> struct VecN<T, 8> : Vec8<T> {};
 
 
+// One lane's EL elements of a row as loaded (unconverted), so that a batch of
+// rows in flight costs EL * sizeof(T) bytes of registers per row.
+template <typename T, int EL> struct Raw;
+template <> struct Raw<uint16_t, 8> {
+  uint4 a;
+  __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    const unsigned int w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Raw<uint16_t, 4> {
+  uint2 a;
+  __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint2 *>(p); }
+  __device__ __forceinline__ void unpack(float (&x)[4]) const {
+    x[0] = __uint_as_float(a.x << 16); x[1] = __uint_as_float(a.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(a.y << 16); x[3] = __uint_as_float(a.y & 0xFFFF0000u);
+  }
+};
+template <int EL> struct Raw<float, EL> {
+  float v[EL];
+  __device__ __forceinline__ void load(const float *p) { VecN<float, EL>::load(p, v); }
+  __device__ __forceinline__ void unpack(float (&x)[EL]) const {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) x[e] = v[e];
+  }
+};
+
 template <typename T, int D, int ML>
 __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v, char *__restrict__ ws, FwdWs w,
@@ -91,6 +109,9 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   constexpr int EL = ML <= 4 ? 8 : 4;   // elements per lane
   constexpr int CH = D / EL;            // threads per row
   constexpr int RG = 256 / CH;          // row-groups per work-group
+  // rows of a window read per batch, two batches in flight (measured: short
+  // windows favour occupancy, long ones more bytes in flight)
+  constexpr int NB = ML <= 3 ? 2 : 8;
   const int h = blockIdx.y;
   const int z = blockIdx.z;             // 0: Q and its scores, 1: K and its scores, 2: V
   const bool scored = z < 2;
@@ -115,65 +136,79 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   unsigned int umin = 0xFFFFFFFFu, umax = 0u;
 
   const long long t0 = win * G;
-  // the rows of the window are read one ahead of their use
+  // the rows of the window are read in batches of NB, one batch ahead of
+  // their use (rows past the window clamp to its last row, unused)
   const long long last = active ? t0 + G - 1 : 0;
-  float nx[EL];
-  VecN<T, EL>::load(x + hoff + (active ? t0 : 0) * D + j * EL, nx);
-  for (int r = 0; r < G; ++r) {
-    const long long t = t0 + r;
-    float xr[EL];
+  const T *xh = x + hoff + j * EL;
+  Raw<T, EL> cur[NB], nxt[NB];
+  auto load_batch = [&](Raw<T, EL>(&b)[NB], int r0) {
 #pragma unroll
-    for (int e = 0; e < EL; ++e) xr[e] = active ? nx[e] : 0.f;
-    VecN<T, EL>::load(x + hoff + (active ? min(t + 1, last) : 0) * D + j * EL, nx);
-    float a = 0.f;
-    if (scored) {
-      float sq = 0.f;
+    for (int u = 0; u < NB; ++u) b[u].load(xh + (active ? min(t0 + r0 + u, last) : 0) * D);
+  };
+  load_batch(cur, 0);
+  for (int r0 = 0; r0 < G; r0 += NB) {
+    if (r0 + NB < G) load_batch(nxt, r0 + NB);
 #pragma unroll
-      for (int e = 0; e < EL; ++e) sq = fmaf(xr[e], xr[e], sq);
+    for (int u = 0; u < NB; ++u) {
+      const int r = r0 + u;
+      if (r >= G) break;
+      const long long t = t0 + r;
+      float xr[EL];
+      cur[u].unpack(xr);
 #pragma unroll
-      for (int m = 1; m < CH; m <<= 1) sq += __shfl_xor(sq, m, CH);
-      a = sqrtf(sq);
-      if (active && j == 0) {
-        sc[t] = a;
-        if (L > 1) {
-          umin = min(umin, __float_as_uint(a));
-          umax = max(umax, __float_as_uint(a));
-        }
-      }
-    }
-    if (L == 1) continue;
-    // level 1 accumulates rows; level l+1 accumulates completed level-l windows
+      for (int e = 0; e < EL; ++e) xr[e] = active ? xr[e] : 0.f;
+      float a = 0.f;
+      if (scored) {
+        float sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[1][e] += xr[e];
-    mx[1] = fmaxf(mx[1], a);
+        for (int e = 0; e < EL; ++e) sq = fmaf(xr[e], xr[e], sq);
 #pragma unroll
-    for (int l = 1; l < ML; ++l) {
-      if (l >= L) break;
-      if (((r + 1) % s.pw[l]) != 0) break;   // window of level l not complete yet
-      const long long i = (t + 1) / s.pw[l] - 1;
-      const float inv = 1.0f / (float)s.pw[l];
-      if (active) {
-        float mean[EL];
-#pragma unroll
-        for (int e = 0; e < EL; ++e) mean[e] = acc[l][e] * inv;
-        VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][z]) + ((long long)h * s.n[l] + i) * D + j * EL, mean);
-        if (scored && j == 0) {
-          sc[s.off[l] + (int)i] = mx[l];
-          if (l <= L - 2) {
-            umin = min(umin, __float_as_uint(mx[l]));
-            umax = max(umax, __float_as_uint(mx[l]));
+        for (int m = 1; m < CH; m <<= 1) sq += __shfl_xor(sq, m, CH);
+        a = sqrtf(sq);
+        if (active && j == 0) {
+          sc[t] = a;
+          if (L > 1) {
+            umin = min(umin, __float_as_uint(a));
+            umax = max(umax, __float_as_uint(a));
           }
         }
       }
-      if (l + 1 < ML && l + 1 < L) {
+      if (L == 1) continue;
+      // level 1 accumulates rows; level l+1 accumulates completed level-l windows
 #pragma unroll
-        for (int e = 0; e < EL; ++e) acc[l + 1][e] += acc[l][e];
-        mx[l + 1] = fmaxf(mx[l + 1], mx[l]);
+      for (int e = 0; e < EL; ++e) acc[1][e] += xr[e];
+      mx[1] = fmaxf(mx[1], a);
+#pragma unroll
+      for (int l = 1; l < ML; ++l) {
+        if (l >= L) break;
+        if (((r + 1) % s.pw[l]) != 0) break;   // window of level l not complete yet
+        const long long i = (t + 1) / s.pw[l] - 1;
+        const float inv = 1.0f / (float)s.pw[l];
+        if (active) {
+          float mean[EL];
+#pragma unroll
+          for (int e = 0; e < EL; ++e) mean[e] = acc[l][e] * inv;
+          VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[l][z]) + ((long long)h * s.n[l] + i) * D + j * EL, mean);
+          if (scored && j == 0) {
+            sc[s.off[l] + (int)i] = mx[l];
+            if (l <= L - 2) {
+              umin = min(umin, __float_as_uint(mx[l]));
+              umax = max(umax, __float_as_uint(mx[l]));
+            }
+          }
+        }
+        if (l + 1 < ML && l + 1 < L) {
+#pragma unroll
+          for (int e = 0; e < EL; ++e) acc[l + 1][e] += acc[l][e];
+          mx[l + 1] = fmaxf(mx[l + 1], mx[l]);
+        }
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[l][e] = 0.f;
+        mx[l] = 0.f;
       }
-#pragma unroll
-      for (int e = 0; e < EL; ++e) acc[l][e] = 0.f;
-      mx[l] = 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) cur[u] = nxt[u];
   }
   if (L == 1 || !scored) return;
   // range of the candidates' score bits over both streams (a key's upper half is
