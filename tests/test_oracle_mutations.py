@@ -1,7 +1,8 @@
 """The oracle's pins catch plausible mistakes: each test plants one mistake in
 the fp64 oracle (on the CPU, through monkeypatch, so the oracle's own internal
-calls see it too), runs every pin of ``test_oracle_pins.py``, and requires at
-least one of them to fail with an AssertionError.
+calls see it too), runs every pin of ``test_oracle_pins.py`` (of
+``test_layer_oracle_pins.py`` for the layer oracle), and requires at least one
+of them to fail with an AssertionError.
 
 The mistakes are the kind a reader of the pages could make: a flipped tie
 order, swapped streams, a dropped factor or scale, an off-by-one window, range
@@ -17,13 +18,15 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.layer_ref as yr
 import oracle.lighthouse_ref as lr
+import test_layer_oracle_pins as layer_pins
 import test_oracle_pins as pins
 
 
-def _pin_calls():
-    """(name, function, kwargs) for every pin, parametrized cases expanded."""
-    for name, f in inspect.getmembers(pins, inspect.isfunction):
+def _pin_calls(module=pins):
+    """(name, function, kwargs) for every pin of ``module``, parametrized cases expanded."""
+    for name, f in inspect.getmembers(module, inspect.isfunction):
         if not name.startswith("test_"):
             continue
         params = set(inspect.signature(f).parameters)
@@ -309,3 +312,77 @@ def test_planted_mistake_fails_a_pin(mut, monkeypatch):
                 caught = name
                 break
     assert caught is not None, f"no pin fails with the planted mistake: {mut.name}"
+
+
+# ---- the projection-inclusive layer (oracle/layer_ref.py) ---------------------
+def _heads_interleaved(z, H):
+    N, Hd = z.shape
+    return z.reshape(N, Hd // H, H).transpose(2, 0, 1)   # mistake: head h = columns h, h + H, ...
+
+
+def _concat_interleaved(z):
+    H, N, d = z.shape
+    return z.transpose(1, 2, 0).reshape(N, H * d)   # the inverse of the interleaved split
+
+
+def _wrap_layer_q_from_wk(orig):
+    def layer_forward(x, wq, wk, wv, wo, H, L, p, topk, flags=None, store=None):
+        return orig(x, wk, wk, wv, wo, H, L, p, topk, flags=flags, store=store)   # mistake: Q = X W_K
+    return layer_forward
+
+
+def _wrap_layer_dx_without_v(orig):
+    def layer_backward(x, wq, wk, wv, wo, dy, H, L, p, flags, store=None):
+        g = orig(x, wq, wk, wv, wo, dy, H, L, p, flags, store)
+        g["dx"] = g["dx"] - yr.concat_heads(g["dv"]) @ np.asarray(wv, dtype=np.float64).T   # mistake: no V path
+        return g
+    return layer_backward
+
+
+def _wrap_layer_dwq_dwk_swapped(orig):
+    def layer_backward(x, wq, wk, wv, wo, dy, H, L, p, flags, store=None):
+        g = orig(x, wq, wk, wv, wo, dy, H, L, p, flags, store)
+        g["dwq"], g["dwk"] = g["dwk"], g["dwq"]   # mistake
+        return g
+    return layer_backward
+
+
+def _wrap_layer_no_wo(orig):
+    def layer_forward(x, wq, wk, wv, wo, H, L, p, topk, flags=None, store=None):
+        r = orig(x, wq, wk, wv, wo, H, L, p, topk, flags=flags, store=store)
+        r["y"] = r["o"] @ np.eye(*np.asarray(wo).shape)   # mistake: W_O replaced by a plain truncation
+        return r
+    return layer_forward
+
+
+LAYER_MUTATIONS = [
+    Mutation("layer: heads interleaved instead of column blocks", "heads_of", lambda o: _heads_interleaved),
+    Mutation("layer: head concat interleaved", "concat_heads", lambda o: _concat_interleaved),
+    Mutation("layer: Q projected with W_K", "layer_forward", _wrap_layer_q_from_wk),
+    Mutation("layer: W_O product dropped", "layer_forward", _wrap_layer_no_wo),
+    Mutation("layer backward: dX misses the V path", "layer_backward", _wrap_layer_dx_without_v),
+    Mutation("layer backward: dW_Q and dW_K swapped", "layer_backward", _wrap_layer_dwq_dwk_swapped),
+]
+
+
+@pytest.mark.parametrize("mut", LAYER_MUTATIONS, ids=[m.name for m in LAYER_MUTATIONS])
+def test_planted_layer_mistake_fails_a_pin(mut, monkeypatch):
+    bad = mut.make(getattr(yr, mut.target))
+    monkeypatch.setattr(yr, mut.target, bad)
+    monkeypatch.setattr(oracle, mut.target, bad)
+    caught = None
+    with np.errstate(all="ignore"):
+        for name, f, kw in _pin_calls(layer_pins):
+            try:
+                f(**kw)
+            except AssertionError:
+                caught = name
+                break
+    assert caught is not None, f"no layer pin fails with the planted mistake: {mut.name}"
+
+
+def test_layer_pins_pass_unmutated():
+    calls = list(_pin_calls(layer_pins))
+    assert len(calls) >= 5
+    for name, f, kw in calls:
+        f(**kw)
