@@ -39,14 +39,6 @@ __device__ __forceinline__ float from_fixed(long long a) {
 
 constexpr int kMaxL = 8;   // levels supported (validated on the host)
 
-// Fixed-point sum of a position's contributions: the sum over its selected
-// entries of RNE(x 2^32) as an integer, converted back with one rounding
-// (* 2^-32 -> fp32 RNE, then bf16 RNE if the output is bf16).  RNE(x 2^32) is
-// an integer that fp32 rintf gives exactly; while every |x| < 2^18 each term is
-// below 2^50 in magnitude and the sum of at most kMaxL of them is exact in
-// fp64, which is then the same integer as the int64 sum (and (double)int64
-// gives the same value): that path is taken unless some |x| >= 2^18, where the
-// int64 sum is formed instead.
 __device__ __forceinline__ void store_row8(void *o, int o_dtype, long long off, const float (&q)[8]) {
   if (o_dtype == LH_BF16) {
     uint4 w;
@@ -137,6 +129,16 @@ constexpr int kScatterGroups = 2;   // groups of 4 positions per thread in k_sca
 //                  output with the full sum, their own row included.
 // Both form the same fixed-point sum, so the result does not depend on which
 // pass wrote a position last.
+//
+// fixed_out: the fixed-point sum of a position's contributions (k_scatter forms
+// the same sum inline), i.e. the sum over its selected entries of RNE(x 2^32)
+// as an integer, converted back with one rounding (* 2^-32 -> fp32 RNE, then
+// bf16 RNE if the output is bf16).  RNE(x 2^32) is
+// an integer that fp32 rintf gives exactly; while every |x| < 2^18 each term is
+// below 2^50 in magnitude and the sum of at most kMaxL of them is exact in
+// fp64, which is then the same integer as the int64 sum (and (double)int64
+// gives the same value): that path is taken unless some |x| >= 2^18, where the
+// int64 sum is formed instead.
 template <int LM>
 __device__ __forceinline__ void fixed_out(const float (&xs)[LM][8], const bool (&has)[LM], float (&q)[8]) {
   bool big = false;
