@@ -223,8 +223,8 @@ def main() -> int:
                          "reference dispatch for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (heads or sequence shards "
-              f"would be split across GPUs; see the design notes)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the library has no "
+              f"multi-GPU path: heads or sequence shards would have to be split across GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np  # noqa: F401

@@ -17,7 +17,7 @@ with Lighthouse Attention"):
                 attention and the gather (``lighthouse_ref.backward_head``), and
                 the chain rule through the two products gives dX and every dW.
 
-Readings (listed with their reasons in the repository's design notes):
+Readings taken where the pages leave a step open:
   * W_O is the output projection of the attention block of the Llama-3-style
     decoder the pages train (experiments paragraph: d_model = 1024, 8 heads of
     head dimension 128); the pages define only W_Q, W_K, W_V (Sec. 3.1).

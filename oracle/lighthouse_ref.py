@@ -35,8 +35,7 @@ on whatever input values it is given (bf16 inputs are passed upcast exactly):
   backward          Paper §3.2: indices are discrete and carry no gradient; the
                     gradient flows through scatter, attention, gather and pool.
 
-Readings taken where the pages leave a step open (each is listed, with its
-reason, in the repository's design notes):
+Readings taken where the pages leave a step open:
   * attention scale 1/sqrt(d) for every entry, pooled or not;
   * scores are l2 norms, not squared norms;
   * selection budget B = min((L-1) p k, |E|) *distinct* entries over the
