@@ -92,6 +92,16 @@ def test_backward_shapes(lh):
     _run_bwd(lh, synth.config("tiny", N=1944, L=3, p=3, k=20, H=1), heads=[0])   # p not a power of two
 
 
+@pytest.mark.parametrize("over", [
+    dict(N=2048, H=2, d=64),                  # bf16 MFMA backward at d = 64
+    dict(N=2048, L=4, p=2, k=16, H=1, d=64),  # p = 2: the one-position-per-thread scatter and pool adjoints
+    dict(N=2048, L=5, p=4, k=8, H=1),         # five levels
+    dict(N=2048, L=6, p=4, k=2, H=1),         # six levels (the widest level template)
+], ids=["d64", "p2-L4", "L5", "L6"])
+def test_backward_shapes_bf16(lh, over):
+    _run_bwd(lh, synth.config("bwd8k", **over), heads=[0])
+
+
 def test_backward_properties_scale_and_determinism(lh):
     import torch
     cfg = synth.config("bwd8k", N=65536, H=2)
