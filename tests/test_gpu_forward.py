@@ -152,6 +152,17 @@ def test_shapes_fp32(lh, N, L, p, k, B, H):
     _run(lh, cfg)
 
 
+@pytest.mark.parametrize("N,L,p,k,d", [
+    (2048, 2, 4, 64, 64),    # two levels
+    (4096, 5, 4, 8, 128),    # five levels, p = 4 (groups of four positions in the scatter)
+    (2048, 6, 4, 4, 128),    # six levels: the widest level templates
+    (1024, 8, 2, 4, 64),     # eight levels, p = 2
+])
+def test_shapes_bf16(lh, N, L, p, k, d):
+    """bf16 storage at the level counts the bf16 workloads do not reach, stage by stage."""
+    _run(lh, synth.config("bwd8k", N=N, L=L, p=p, k=k, H=1, d=d))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_small_bf16(lh, d):
     cfg = synth.config("bwd8k", N=4096, H=2, d=d)
