@@ -231,10 +231,43 @@ def _check(st, where):
         raise LighthouseError(st, where)
 
 
-def _shape(q):
-    if q.dim() != 4 or not q.is_contiguous():
-        raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors")
+def _require(name, t, shape=None, dtype=None, device=None):
+    """Refuse, before anything reaches the library, a buffer its kernels would
+    misread or fault on: not a device tensor, on another device, of another
+    shape or dtype, or not contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got one on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _require_bytes(name, t, device):
+    if t is not None:
+        _require(name, t, dtype=torch.uint8, device=device)
+
+
+def _shape(q, k, v):
+    """[B, H, N, d] of q, with k and v required to match it."""
+    _require("q", q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be a [B, H, N, d] tensor, got shape {tuple(q.shape)}")
+    for name, t in (("k", k), ("v", v)):
+        _require(name, t, q.shape, q.dtype, q.device)
     return q.shape
+
+
+def _same_problem(plan, B, H, N, d, io):
+    got = (plan.B, plan.H, plan.N, plan.d, plan.io)
+    if got != (B, H, N, d, dtype_code(io)):
+        raise ValueError(f"plan was made for (B, H, N, d, io) = {got}, not for these inputs")
 
 
 class Plan:
@@ -255,10 +288,13 @@ class Plan:
 
 def forward(q, k, v, L, p, topk, out_dtype=None, saved=None, ws=None, plan=None):
     """O = Lighthouse(q, k, v).  Returns (o, saved, plan); `saved` feeds backward."""
-    B, H, N, d = _shape(q)
-    plan = plan or Plan(B, H, N, d, L, p, topk, q.dtype)
-    out_dtype = out_dtype or q.dtype
+    B, H, N, d = _shape(q, k, v)
     dev = q.device
+    _require_bytes("saved", saved, dev)
+    _require_bytes("ws", ws, dev)
+    plan = plan or Plan(B, H, N, d, L, p, topk, q.dtype)
+    _same_problem(plan, B, H, N, d, q.dtype)
+    out_dtype = out_dtype or q.dtype
     o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
     if saved is None:
         saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=dev)
@@ -272,15 +308,20 @@ def forward(q, k, v, L, p, topk, out_dtype=None, saved=None, ws=None, plan=None)
 
 def backward(q, k, v, dout, saved, plan, grad_dtype=None, ws=None):
     """(dq, dk, dv) with the forward's selection frozen."""
-    B, H, N, d = _shape(q)
-    grad_dtype = grad_dtype or q.dtype
+    B, H, N, d = _shape(q, k, v)
     dev = q.device
+    dout = dout.contiguous()
+    _require("dout", dout, q.shape, device=dev)
+    _require_bytes("saved", saved, dev)
+    _require_bytes("ws", ws, dev)
+    _same_problem(plan, B, H, N, d, q.dtype)
+    grad_dtype = grad_dtype or q.dtype
     dq = torch.empty((B, H, N, d), dtype=grad_dtype, device=dev)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     if ws is None:
         ws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
-    st = lh_backward(q, k, v, dout.contiguous(), dtype_code(dout.dtype), saved, saved.numel(), dq, dk, dv,
+    st = lh_backward(q, k, v, dout, dtype_code(dout.dtype), saved, saved.numel(), dq, dk, dv,
                      dtype_code(grad_dtype), *plan.args()[:7], plan.io, ws, ws.numel())
     _check(st, "lh_backward")
     return dq, dk, dv
@@ -353,11 +394,34 @@ class LayerPlan:
         return saved[off:off + n * (2 if self.io == LH_BF16 else 4)].view(io).view(self.B, self.H, self.N, self.d)
 
 
+def _layer_shape(x, wq, wk, wv, wo, H):
+    """(B, N, d_model, d) of the layer, with every operand checked against x."""
+    _require("x", x)
+    if x.dim() != 3:
+        raise ValueError(f"x must be a [B, N, d_model] tensor, got shape {tuple(x.shape)}")
+    B, N, dm = x.shape
+    if wq.dim() != 2 or wq.shape[1] % H:
+        raise ValueError(f"wq must be [d_model, H d] with H = {H}, got shape {tuple(wq.shape)}")
+    d = wq.shape[1] // H
+    for name, w, shape in (("wq", wq, (dm, H * d)), ("wk", wk, (dm, H * d)), ("wv", wv, (dm, H * d)),
+                           ("wo", wo, (H * d, dm))):
+        _require(name, w, shape, x.dtype, x.device)
+    return B, N, dm, d
+
+
+def _same_layer(plan, B, H, N, dm, d, io):
+    got = (plan.B, plan.H, plan.N, plan.d_model, plan.d, plan.io)
+    if got != (B, H, N, dm, d, dtype_code(io)):
+        raise ValueError(f"plan was made for (B, H, N, d_model, d, io) = {got}, not for these inputs")
+
+
 def layer_forward(x, wq, wk, wv, wo, H, L, p, topk, y_dtype=None, plan=None, saved=None, ws=None):
     """Y of the layer for x [B, N, d_model].  Returns (y, saved, plan)."""
-    B, N, dm = x.shape
-    d = wq.shape[1] // H
+    B, N, dm, d = _layer_shape(x, wq, wk, wv, wo, H)
+    _require_bytes("saved", saved, x.device)
+    _require_bytes("ws", ws, x.device)
     plan = plan or LayerPlan(B, H, N, dm, d, L, p, topk, x.dtype)
+    _same_layer(plan, B, H, N, dm, d, x.dtype)
     y_dtype = y_dtype or x.dtype
     y = torch.empty((B, N, dm), dtype=y_dtype, device=x.device)
     if saved is None:
@@ -371,13 +435,19 @@ def layer_forward(x, wq, wk, wv, wo, H, L, p, topk, y_dtype=None, plan=None, sav
 
 def layer_backward(x, wq, wk, wv, wo, dy, saved, plan, dx_dtype=None, ws=None):
     """(dx, dwq, dwk, dwv, dwo) with the forward's selection frozen."""
+    B, N, dm, d = _layer_shape(x, wq, wk, wv, wo, plan.H)
+    dy = dy.contiguous()
+    _require("dy", dy, x.shape, x.dtype, x.device)
+    _require_bytes("saved", saved, x.device)
+    _require_bytes("ws", ws, x.device)
+    _same_layer(plan, B, plan.H, N, dm, d, x.dtype)
     dx_dtype = dx_dtype or x.dtype
     dev = x.device
     dx = torch.empty(x.shape, dtype=dx_dtype, device=dev)
     dws = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in (wq, wk, wv, wo)]
     if ws is None:
         ws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
-    st = lh_layer_backward(x, wq, wk, wv, wo, dy.contiguous(), saved, saved.numel(), dx, dx_dtype, *dws,
+    st = lh_layer_backward(x, wq, wk, wv, wo, dy, saved, saved.numel(), dx, dx_dtype, *dws,
                            *plan.args(), ws, ws.numel())
     _check(st, "lh_layer_backward")
     return (dx, *dws)

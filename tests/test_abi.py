@@ -185,3 +185,18 @@ def test_layer_validation_before_launch(lh):
                                 bws) == 1
     assert lh.library().lh_layer_backward(*head, fake, saved, fake, 9, *grads, B, H, N, dm, d, L, p, k, 0, fake, bws,
                                           None) == 1
+
+
+def test_binding_refuses_host_tensors(lh):
+    """The convenience wrappers refuse host tensors before anything reaches the
+    library (a host pointer handed to a kernel would fault the GPU)."""
+    import torch
+    q = torch.zeros((1, 2, 1024, 64))
+    with pytest.raises(ValueError, match="device"):
+        lh.forward(q, q, q, 3, 4, 64)
+    with pytest.raises(ValueError, match="device"):
+        lh.backward(q, q, q, q, torch.zeros(16, dtype=torch.uint8), lh.Plan(1, 2, 1024, 64, 3, 4, 64, "f32"))
+    x = torch.zeros((1, 1024, 128))
+    w = torch.zeros((128, 128))
+    with pytest.raises(ValueError, match="device"):
+        lh.layer_forward(x, w, w, w, w, 2, 3, 4, 64)

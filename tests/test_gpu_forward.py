@@ -29,7 +29,7 @@ import numpy as np
 import pytest
 
 import oracle as orc
-from gpu_helpers import gpu_head, head_inputs_f64, run_forward, say, split_levels
+from gpu_helpers import gpu_head, head_inputs_f64, run_forward, say, split_levels, to_dev
 from hierarchical_sparse_attention_mean_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -280,3 +280,28 @@ def test_scatter_large_values(lh, N, L, p):
         assert big.any() and (~big).any()
         o_fx = orc.scatter_fixed(g["ot32"].astype(np.float64), g["coords"], N, L, p, "f32")
         assert np.array_equal(o_fx, g["o"]), "scatter not bit-exact"
+
+
+def test_binding_refuses_mismatched_operands(lh):
+    """Operands the kernels would misread are refused by the binding: another
+    dtype or shape than q, a plan made for another problem, host buffers."""
+    import torch
+    cfg = synth.config("bwd8k", N=2048, H=2)
+    inp = synth.make_inputs(cfg, with_do=True)
+    run = run_forward(lh, cfg, inp)
+    q, k, v = run["q"], run["k"], run["v"]
+    L, p, topk = cfg["L"], cfg["p"], cfg["k"]
+    with pytest.raises(ValueError, match="dtype"):
+        lh.forward(q, k.float(), v, L, p, topk)
+    with pytest.raises(ValueError, match="shape"):
+        lh.forward(q, k, v[:, :1].contiguous(), L, p, topk)
+    other = lh.Plan(cfg["B"], cfg["H"], 4096, cfg["d"], L, p, topk, q.dtype)
+    with pytest.raises(ValueError, match="plan"):
+        lh.forward(q, k, v, L, p, topk, plan=other)
+    dout = to_dev(inp["do"], cfg["dtype"])
+    with pytest.raises(ValueError, match="device"):
+        lh.backward(q, k, v, dout.cpu(), run["saved"], run["plan"])
+    with pytest.raises(ValueError, match="device"):
+        lh.backward(q, k, v, dout, run["saved"].cpu(), run["plan"])
+    with pytest.raises(ValueError, match="plan"):
+        lh.backward(q, k, v, dout, run["saved"], other)
