@@ -7,6 +7,7 @@ already resident in HBM.  Default workload: B=1, H=8, d=128, N=524,288, L=3,
 p=4, k=4,096 (S=65,536).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 512k] [--no-dense] [--layer]
+    python bench.py --ablation [--steps K] [--warmup W]     (the ablation grid at N = 98,304)
 
 Prints one JSON line (rank 0).  Besides the contract fields it carries:
   roofline      the dominant kernel of the step (by time): its algorithmic FLOPs
@@ -107,6 +108,161 @@ def counter_traffic(stage: str, config: str):
     if not all(m.values()) or m["source_sha256"].group(1) != sources_sha256(ATTN_STAGES[stage][1]):
         return None
     return float(m["fetch_bytes_per_launch"].group(1)) + float(m["write_bytes_per_launch"].group(1))
+
+
+def time_lighthouse(lh, torch, x, cfg: dict, steps: int, warmup: int, copy_mib: int = 0) -> dict:
+    """Times the layer (forward + backward) of workload `cfg` on the resident
+    inputs x = (q, k, v, dO): `warmup` untimed steps, then `steps` timed ones
+    with the library's stage timing on, then `steps` forward-only ones.
+    Returns S, ms per step, forward-only ms and the per-stage records (ms per
+    step and per launch; TFLOP/s of the MFMA stages; algorithmic bytes, GB/s
+    and fraction of the HBM peak of the memory-bound stages).  `copy_mib` runs
+    one plain device copy of that size before the timed steps (a known-size
+    reference dispatch for hardware byte counters)."""
+    q, kk, v, do = x
+    B, H, N, d, L, p, k = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["L"], cfg["p"], cfg["k"]
+    BH, io, dev = B * H, q.dtype, q.device
+    plan = lh.Plan(B, H, N, d, L, p, k, io)
+    S = plan.S
+    o = torch.empty((B, H, N, d), dtype=io, device=dev)
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=io, device=dev) for _ in range(3))
+    saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=dev)
+    fws = torch.empty(plan.fwd_ws_bytes, dtype=torch.uint8, device=dev)
+    bws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+    a7 = plan.args()
+
+    def fwd():
+        st = lh.lh_forward(q, kk, v, o, io, *a7[:7], a7[7], saved, saved.numel(), fws, fws.numel())
+        if st:
+            raise lh.LighthouseError(st, "lh_forward")
+
+    def bwd():
+        st = lh.lh_backward(q, kk, v, do, io, saved, saved.numel(), dq, dk, dv, io, *a7[:7], a7[7], bws,
+                            bws.numel())
+        if st:
+            raise lh.LighthouseError(st, "lh_backward")
+
+    for i in range(warmup):
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{warmup} done")
+    if copy_mib:
+        src = torch.ones(copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy: {copy_mib} MiB read, {copy_mib} MiB written")
+        del src, dst
+    torch.cuda.synchronize()
+    lh.lh_timing_begin()   # events around each stage's launches, on their stream
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st, stages = lh.lh_timing_end()
+    if st:
+        raise lh.LighthouseError(st, "lh_timing_end")
+    ms = (t1 - t0) * 1e3 / steps
+    log(f"[bench] {steps} steps: {ms:.3f} ms/step")
+    stage_ms = {n: {"ms_per_step": t / steps, "ms_per_launch": t / c if c else None, "launches_per_step": c / steps}
+                for n, (t, c) in stages.items()}
+    for n, rec in stage_ms.items():
+        log(f"[bench]   {n:14s} {rec['ms_per_step']:8.3f} ms/step")
+
+    # forward alone
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    ms_fwd = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] forward only: {ms_fwd:.3f} ms")
+
+    for n in ATTN_STAGES:
+        rec = stage_ms[n]
+        if rec["ms_per_launch"]:
+            rec["tflops"] = attention_flops(S, d, BH, ATTN_STAGES[n][0]) / (rec["ms_per_launch"] * 1e-3) / 1e12
+    for n, nbytes in hbm_stage_bytes(cfg, S).items():
+        rec = stage_ms[n]
+        if rec["ms_per_step"] > 0:
+            rec["algorithmic_bytes"] = nbytes
+            rec["gbs"] = nbytes / (rec["ms_per_step"] * 1e-3) / 1e9
+            rec["frac_of_hbm_peak"] = rec["gbs"] / PEAK_HBM_GBS
+            log(f"[bench]   {n:14s} {rec['gbs']:8.0f} GB/s ({rec['frac_of_hbm_peak']:.0%} of {PEAK_HBM_GBS:.0f})")
+    return {"S": S, "ms": ms, "ms_fwd": ms_fwd, "stages": stage_ms}
+
+
+def resident_inputs(torch, np, synth, cfg: dict, name: str, dev):
+    """The workload's seeded q, k, v, dO as device tensors (bf16 or fp32)."""
+    log(f"[bench] generating {name} inputs (B={cfg['B']} H={cfg['H']} N={cfg['N']} d={cfg['d']})")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(cfg, with_do=True)
+    out = []
+    for n in ("q", "k", "v", "do"):
+        a = inp.pop(n)
+        if cfg["dtype"] == "bf16":
+            out.append(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev))
+        else:
+            out.append(torch.from_numpy(a).to(dev))
+        del a
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    return tuple(out)
+
+
+# The pages' ablation axes -- budget k, pooling factor p, levels L -- each varied
+# on its own around one default cell (L = 3, p = 4, k = 1536), at the training
+# shape N = 98,304, B = 1, H = 8, d = 128, bf16.  The p = 2 axis is taken at both
+# budgets the pages name for it (1536 and 4096).
+ABLATION_GRID = [
+    (3, 4, 1536), (3, 4, 2048), (3, 4, 3072), (3, 4, 4096), (3, 4, 6144),
+    (3, 2, 1536), (3, 2, 4096),
+    (4, 4, 1536), (5, 4, 1536),
+]
+
+
+def run_ablation(args, torch, np, lh, synth) -> int:
+    """Forward + backward over ABLATION_GRID on the same resident inputs; one
+    JSON line whose value is the default cell's tokens/s and whose extra.grid
+    holds every cell (S, ms per step, forward ms, tokens/s, TFLOP/s of the
+    attention kernels, fraction of the HBM peak of the memory-bound stages)."""
+    base = synth.config("98k")
+    B, N = base["B"], base["N"]
+    x = resident_inputs(torch, np, synth, base, "98k", torch.device("cuda:0"))
+    grid = []
+    for L, p, k in ABLATION_GRID:
+        cfg = synth.config("98k", L=L, p=p, k=k)
+        log(f"[bench] ablation cell L={L} p={p} k={k}")
+        r = time_lighthouse(lh, torch, x, cfg, args.steps, args.warmup)
+        st = r["stages"]
+        grid.append({"L": L, "p": p, "k": k, "S": r["S"], "ms_per_step": r["ms"], "ms_forward": r["ms_fwd"],
+                     "tokens_per_s": B * N / (r["ms"] * 1e-3),
+                     "attn_tflops": {n: st[n].get("tflops") for n in ATTN_STAGES},
+                     "hbm_frac_of_peak": {n: st[n].get("frac_of_hbm_peak") for n in hbm_stage_bytes(cfg, r["S"])}})
+    d0 = grid[0]
+    line = {
+        "metric": "Lighthouse fwd+bwd tokens/s over the ablation grid at N=98,304, H=8, d=128",
+        "value": d0["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": d0["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Lighthouse layer fwd+bwd over the ablation grid (L, p, k) at B=1 H=8 d=128 "
+                               "N=98304; value at L=3 p=4 k=1536", "B": B, "H": base["H"], "d": base["d"], "N": N},
+        "roofline": None,
+        "cpu_baseline": None,
+        "extra": {"grid": grid},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def cpu_baseline(cfg: dict) -> dict:
@@ -218,6 +374,8 @@ def main() -> int:
     ap.add_argument("--layer", action="store_true",
                     help="also time the projection-inclusive layer (W_Q, W_K, W_V, W_O around the attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time forward + backward over the ablation grid at N = 98,304 instead (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps (a known-size "
                          "reference dispatch for hardware byte counters)")
@@ -233,84 +391,17 @@ def main() -> int:
     from hierarchical_sparse_attention_mean_amd import lighthouse as lh
     from hierarchical_sparse_attention_mean_amd import synth
 
+    if args.ablation:
+        return run_ablation(args, torch, np, lh, synth)
+
     cfg = synth.config(args.config)
     B, H, N, d, L, p, k = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["L"], cfg["p"], cfg["k"]
     BH = B * H
     dev = torch.device("cuda:0")
-    log(f"[bench] generating {args.config} inputs (B={B} H={H} N={N} d={d})")
-    t0 = time.perf_counter()
-    inp = synth.make_inputs(cfg, with_do=True)
-    tens = {}
-    for n in ("q", "k", "v", "do"):
-        a = inp.pop(n)
-        if cfg["dtype"] == "bf16":
-            tens[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        else:
-            tens[n] = torch.from_numpy(a).to(dev)
-        del a
-    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
-    q, kk, v, do = tens["q"], tens["k"], tens["v"], tens["do"]
+    q, kk, v, do = resident_inputs(torch, np, synth, cfg, args.config, dev)
     io = q.dtype
-    plan = lh.Plan(B, H, N, d, L, p, k, io)
-    S = plan.S
-    o = torch.empty((B, H, N, d), dtype=io, device=dev)
-    dq, dk, dv = (torch.empty((B, H, N, d), dtype=io, device=dev) for _ in range(3))
-    saved = torch.empty(plan.saved_bytes, dtype=torch.uint8, device=dev)
-    fws = torch.empty(plan.fwd_ws_bytes, dtype=torch.uint8, device=dev)
-    bws = torch.empty(plan.bwd_ws_bytes, dtype=torch.uint8, device=dev)
-    a7 = plan.args()
-
-    def fwd():
-        st = lh.lh_forward(q, kk, v, o, io, *a7[:7], a7[7], saved, saved.numel(), fws, fws.numel())
-        if st:
-            raise lh.LighthouseError(st, "lh_forward")
-
-    def bwd():
-        st = lh.lh_backward(q, kk, v, do, io, saved, saved.numel(), dq, dk, dv, io, *a7[:7], a7[7], bws,
-                            bws.numel())
-        if st:
-            raise lh.LighthouseError(st, "lh_backward")
-
-    def step():
-        fwd()
-        bwd()
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
-    if args.copy_mib:
-        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] reference copy: {args.copy_mib} MiB read, {args.copy_mib} MiB written")
-        del src, dst
-    torch.cuda.synchronize()
-    lh.lh_timing_begin()   # events around each stage's launches, on their stream
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    st, stages = lh.lh_timing_end()
-    if st:
-        raise lh.LighthouseError(st, "lh_timing_end")
-    ms = (t1 - t0) * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step")
-    stage_ms = {n: {"ms_per_step": t / args.steps, "ms_per_launch": t / c if c else None, "launches_per_step": c / args.steps}
-                for n, (t, c) in stages.items()}
-    for n, rec in stage_ms.items():
-        log(f"[bench]   {n:14s} {rec['ms_per_step']:8.3f} ms/step")
-
-    # forward alone
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        fwd()
-    torch.cuda.synchronize()
-    ms_fwd = (time.perf_counter() - t0) * 1e3 / args.steps
-    log(f"[bench] forward only: {ms_fwd:.3f} ms")
+    run = time_lighthouse(lh, torch, (q, kk, v, do), cfg, args.steps, args.warmup, args.copy_mib)
+    S, ms, ms_fwd, stage_ms = run["S"], run["ms"], run["ms_fwd"], run["stages"]
 
     # dominant kernel: the MFMA attention stage with the most time per step
     dom = max(ATTN_STAGES, key=lambda n: stage_ms[n]["ms_per_step"])
@@ -319,18 +410,6 @@ def main() -> int:
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic = counter_traffic(dom, args.config)
     log(f"[bench] dominant kernel {dom}: {dom_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s")
-    for n in ATTN_STAGES:
-        rec = stage_ms[n]
-        if rec["ms_per_launch"]:
-            rec["tflops"] = attention_flops(S, d, BH, ATTN_STAGES[n][0]) / (rec["ms_per_launch"] * 1e-3) / 1e12
-
-    for n, nbytes in hbm_stage_bytes(cfg, S).items():
-        rec = stage_ms[n]
-        if rec["ms_per_step"] > 0:
-            rec["algorithmic_bytes"] = nbytes
-            rec["gbs"] = nbytes / (rec["ms_per_step"] * 1e-3) / 1e9
-            rec["frac_of_hbm_peak"] = rec["gbs"] / PEAK_HBM_GBS
-            log(f"[bench]   {n:14s} {rec['gbs']:8.0f} GB/s ({rec['frac_of_hbm_peak']:.0%} of {PEAK_HBM_GBS:.0f})")
 
     extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "stages": stage_ms,
              "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
@@ -366,7 +445,6 @@ def main() -> int:
         del od, lsed, grads, wsd
 
     if args.layer:
-        del o, dq, dk, dv
         extra["layer"] = time_layer(lh, synth, cfg, args, dev)
 
     cpu = None
