@@ -22,6 +22,8 @@
 //   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m;
 //   k_pool_bwd     dX_t = sum_l [entry (l, floor(t/p^l)) selected] dX~_slot / p^l
 //                  for X in {Q, K, V} (gather adjoint fused with pool adjoint).
+#include <type_traits>
+
 #include "lh_internal.h"
 
 namespace lh {
@@ -285,13 +287,16 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
     const long long base = ((long long)h * s.N) * D + c * 8;
     if (dout_dtype == LH_BF16) {
       const uint16_t *src = reinterpret_cast<const uint16_t *>(dout) + base;
-      int t = lo;
-      for (; t + 3 <= hi; t += 4) {
-        uint4 w[4];
+      // rows t ascending, 16 rows in flight while at least 16 remain, then 4,
+      // then 1 (ranges of 16 rows and more are the coarser levels'): the
+      // additions are the same, in the same order
+      auto rows_bf16 = [&](int t0, auto n) {
+        constexpr int R = decltype(n)::value;
+        uint4 w[R];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const uint4 *>(src + (long long)(t + u) * D);
+        for (int u = 0; u < R; ++u) w[u] = *reinterpret_cast<const uint4 *>(src + (long long)(t0 + u) * D);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < R; ++u) {
           const unsigned v[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -299,7 +304,10 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
             acc[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
           }
         }
-      }
+      };
+      int t = lo;
+      for (; t + 15 <= hi; t += 16) rows_bf16(t, std::integral_constant<int, 16>{});
+      for (; t + 3 <= hi; t += 4) rows_bf16(t, std::integral_constant<int, 4>{});
       for (; t <= hi; ++t) {
         const uint4 w = *reinterpret_cast<const uint4 *>(src + (long long)t * D);
         const unsigned v[4] = {w.x, w.y, w.z, w.w};
