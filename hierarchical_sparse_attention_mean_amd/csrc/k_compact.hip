@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
                                                             int *__restrict__ coords, T *__restrict__ qt,
                                                             T *__restrict__ kt, T *__restrict__ vt) {
   __shared__ int red[kThreads / 64];
-  __shared__ int scan[kThreads];
+  __shared__ int scan[kThreads / 64];   // wavefront totals
   __shared__ int lflat[kCompactTile * 2];     // flat indices of this tile's slots (spills to global if more)
   const int h = blockIdx.y;
   const int tile = blockIdx.x;
@@ -84,16 +84,24 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
     cnt[e] = (t0 + e < s.N) ? count_at(s, fl, t0 + e) : 0;
     mine += cnt[e];
   }
-  scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
+  // exclusive scan over the block: inclusive scan within each wavefront by
+  // shuffles, then the wavefront totals (one barrier)
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  const int ntot = scan[kThreads - 1];
-  int m = m0 + scan[tid] - mine;
+  if (lane == 63) scan[wv] = incl;
+  __syncthreads();
+  int wbase = 0, ntot = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    wbase += i < wv ? scan[i] : 0;
+    ntot += scan[i];
+  }
+  int m = m0 + wbase + incl - mine;
   int *sl = slot + (long long)h * s.P;
   int *co = coords + (long long)h * s.S;
   for (int e = 0; e < kPer; ++e) {
