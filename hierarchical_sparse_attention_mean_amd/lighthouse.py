@@ -19,7 +19,9 @@ import re
 import torch  # noqa: F401  (must load torch's HIP runtime before the library)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblighthouse.so")
+# LH_LIBRARY names another build of the same library (e.g. a host-side
+# sanitizer build for the host-only tests); default: the in-tree build
+LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_HERE, "liblighthouse.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "lighthouse.h")
 
 if not os.path.exists(LIB_PATH):

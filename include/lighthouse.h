@@ -47,7 +47,16 @@
 extern "C" {
 #endif
 
-typedef enum { LH_F32 = 0, LH_BF16 = 1 } lh_dtype;
+/* Element types.  The two range enumerators are not dtypes: they make every
+ * 32-bit int a value of lh_dtype, so that an invalid dtype argument from a C
+ * caller is an ordinary value that validation rejects with LH_EINVAL rather than
+ * undefined behaviour in the C++ implementation. */
+typedef enum {
+  LH_F32 = 0,
+  LH_BF16 = 1,
+  LH_DTYPE_RANGE_MIN = -2147483647 - 1,
+  LH_DTYPE_RANGE_MAX = 2147483647
+} lh_dtype;
 
 typedef enum {
   LH_OK = 0,
