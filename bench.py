@@ -272,11 +272,13 @@ def cpu_baseline(cfg: dict) -> dict:
     import oracle as orc
     from hierarchical_sparse_attention_mean_amd import synth
 
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        blas = None
+    cores = blas or affinity   # the BLAS products are the oracle's only multi-threaded work
     one = synth.make_inputs(cfg, with_do=True, heads=[0])
     q, k, v, do = (synth.as_f64(one[n][0], cfg["dtype"]) for n in ("q", "k", "v", "do"))
     t0 = time.perf_counter()
@@ -287,6 +289,7 @@ def cpu_baseline(cfg: dict) -> dict:
     per_head = t2 - t0
     layer_s = per_head * cfg["B"] * cfg["H"]
     return {"value": cfg["B"] * cfg["N"] / layer_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_count": os.cpu_count(), "affinity_cores": affinity, "blas_threads": blas,
             "sample": f"head 0 of {cfg['B'] * cfg['H']}, full forward ({t1 - t0:.1f} s) + backward ({t2 - t1:.1f} s) "
                       f"in fp64 numpy; layer time = per-head time x {cfg['B'] * cfg['H']} heads",
             "ms_per_step": layer_s * 1e3}

@@ -14,13 +14,15 @@
 //                    dP^T = V~ dO~^T (lane = one query), dS^T in registers, and
 //                    accumulates dQ^T += K~^T dS^T with K~^T from LDS.
 //                    8 wavefronts, 256 queries per work-group.
-//   k_attn_bwd_dkdv  key-stationary: a wavefront holds 32 key rows of K~ and V~
-//                    as B operands; per 32-query tile it forms S = Q~ K~^T and
-//                    dP = dO~ V~^T (lane = one key), and accumulates
-//                    dV^T += dO~^T P and dK^T += Q~^T dS with the transposed
-//                    query-side operands from LDS.  4 wavefronts, 128 keys per
-//                    work-group (the accumulators need the register file of a
-//                    whole SIMD).
+//   k_attn_bwd_dkdv  key-stationary: the work of 32 keys is split over a pair
+//                    of wavefronts on one SIMD.  The "P" wavefront holds the
+//                    keys' K~ rows and dV~ accumulators: per 32-query tile it
+//                    forms S = Q~ K~^T (lane = one key), P, and
+//                    dV^T += dO~^T P.  The "dS" wavefront holds their V~ rows
+//                    and dK~ accumulators: it forms dP = dO~ V~^T, takes P from
+//                    its partner through LDS, and accumulates dK^T += Q~^T dS.
+//                    The transposed query-side operands come from LDS.  4 pairs
+//                    (8 wavefronts), 128 keys per work-group.
 // Both stream their tiles through LDS filled by direct global->LDS loads
 // (attn_tiles.h) while earlier tiles are computed.  Operands contracted over
 // keys or queries (K~^T, Q~^T, dO~^T) come from the row-major tiles by
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void k_attn_bwd_dkdv(int S, int Sv, 
   constexpr int KC = D / 16, DB = D / 32;
   static_assert(4 * DB == 2 * KC, "as many dV/dK products as S/dP products");
   constexpr int QB = kKvBQ * T::WR / 1024;   // 1 KB fill blocks of a Q~ or dO~ tile
-  static_assert(QB * 1024 == kKvBQ * T::WR && kKvWaves % QB == 0 || QB % kKvWaves == 0, "fill blocks");
+  static_assert(QB * 1024 == kKvBQ * T::WR && (kKvWaves % QB == 0 || QB % kKvWaves == 0), "fill blocks");
   constexpr int QBLK = (QB + kKvWaves - 1) / kKvWaves;   // blocks per wavefront (duplicated if QB < 8)
   constexpr int kFillOps = 2 * QBLK + 1;                  // loads per wavefront per fill
   __shared__ __attribute__((aligned(1024))) char lds[kKvBufs * T::BYTES + 2 * kKvPairs * kXBytes];

@@ -138,11 +138,13 @@ lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
   }
   s->P = (int)acc;
   s->E = (int)(acc - s->n[L - 1]);
-  // budget (L-1) p k, saturating, capped by the candidates
-  int64_t budget = s->E;
-  if (topk < ((int64_t)1 << 40)) {
-    const int64_t b = (int64_t)(L - 1) * p * topk;
-    if (b < budget) budget = b;
+  // budget (L-1) p k capped by the candidates, decided without forming the
+  // product when it would exceed them (so it cannot overflow): per <= 7 (2^31 - 1),
+  // and below the cap per * topk < E + per
+  int64_t budget = 0;
+  if (L > 1) {
+    const int64_t per = (int64_t)(L - 1) * p;
+    budget = (topk >= (s->E + per - 1) / per) ? s->E : per * topk;
   }
   s->Bsel = (int)budget;
   s->S = s->n[L - 1] + s->Bsel;

@@ -350,19 +350,26 @@ def saved_view(saved, plan, name):
 
 
 class LighthouseAttention(torch.autograd.Function):
-    """autograd wrapper: forward and backward both run in liblighthouse."""
+    """autograd wrapper: forward and backward both run in liblighthouse.
+
+    q, k, v may be any strided [B, H, N, d] views (e.g. [B, N, H, d] tensors
+    transposed): the library is given contiguous copies, and those copies (the
+    inputs themselves when already contiguous) are what the backward receives,
+    so it sees exactly the operands the forward ran on.  The gradients come
+    back contiguous in the [B, H, N, d] shape of the inputs."""
 
     @staticmethod
     def forward(ctx, q, k, v, L, p, topk):
-        o, saved, plan = forward(q.contiguous(), k.contiguous(), v.contiguous(), L, p, topk)
-        ctx.save_for_backward(q, k, v, saved)
+        qc, kc, vc = q.contiguous(), k.contiguous(), v.contiguous()
+        o, saved, plan = forward(qc, kc, vc, L, p, topk)
+        ctx.save_for_backward(qc, kc, vc, saved)
         ctx.plan = plan
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, saved = ctx.saved_tensors
-        dq, dk, dv = backward(q, k, v, do, saved, ctx.plan)
+        qc, kc, vc, saved = ctx.saved_tensors
+        dq, dk, dv = backward(qc, kc, vc, do.contiguous(), saved, ctx.plan)
         return dq, dk, dv, None, None, None
 
 

@@ -25,8 +25,10 @@ Readings taken where the pages leave a step open:
     directly on the projections (Sec. 3.2).
   * bf16 mode (``store="bf16"``): every tensor the layer stores between its
     steps -- Q, K, V after the projection, O before W_O, dO after dY W_O^T, and
-    dQ, dK, dV after the attention backward -- is rounded to bf16 once; the
-    products themselves are exact (fp64) here.
+    dQ, dK, dV after the attention backward -- is rounded to bf16 once, and the
+    attention's pooled levels are stored in bf16 in the forward and in the
+    backward alike (``backward_head(store=...)``); the products themselves are
+    exact (fp64) here.
 
 Every function has a pin in ``tests/test_layer_oracle_pins.py``: a textbook
 multi-head attention layer (L = 1), a wiring check with permutation weights,
@@ -84,7 +86,7 @@ def layer_backward(x, wq, wk, wv, wo, dy, H: int, L: int, p: int, flags, store: 
     fw = layer_forward(x, wq, wk, wv, wo, H, L, p, 0, flags=flags, store=store)
     dwo = fw["o"].T @ dy                              # Y = O W_O
     do = heads_of(_store(dy @ wo.T, store), H)
-    g = [backward_head(fw["q"][h], fw["k"][h], fw["v"][h], do[h], L, p, np.asarray(flags[h], dtype=bool))
+    g = [backward_head(fw["q"][h], fw["k"][h], fw["v"][h], do[h], L, p, np.asarray(flags[h], dtype=bool), store)
          for h in range(H)]
     dq, dk, dv = (np.stack([_store(gh[i], store) for gh in g]) for i in range(3))
     dqc, dkc, dvc = concat_heads(dq), concat_heads(dk), concat_heads(dv)

@@ -416,9 +416,16 @@ def pool_adjoint(dlevels: list[np.ndarray], N: int, p: int) -> np.ndarray:
     return out
 
 
-def backward_head(q, k, v, do, L: int, p: int, flags: np.ndarray):
+def backward_head(q, k, v, do, L: int, p: int, flags: np.ndarray, store: str | None = None):
     """(dQ, dK, dV) of sum(O * dO) for one head with the selection ``flags``
-    frozen: no gradient reaches the scores."""
+    frozen: no gradient reaches the scores.
+
+    ``store="bf16"`` differentiates the bf16-mode forward of ``forward_head``:
+    the attention adjoint is taken at the gathered rows as that forward stores
+    them (pooled levels rounded to bf16), and the rounding itself passes the
+    gradient through unchanged -- it is the gradient of the forward whose
+    pooled levels carry their rounding offsets, taken at the base point, as
+    constants."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -426,9 +433,9 @@ def backward_head(q, k, v, do, L: int, p: int, flags: np.ndarray):
     N, d = q.shape
     sizes = level_sizes(N, L, p)
     sorted_flat = order(flags, N, L, p)
-    qt = gather(pyramid(q, L, p), sorted_flat, N, L, p)
-    kt = gather(pyramid(k, L, p), sorted_flat, N, L, p)
-    vt = gather(pyramid(v, L, p), sorted_flat, N, L, p)
+    qt = gather(pyramid(q, L, p, store), sorted_flat, N, L, p)
+    kt = gather(pyramid(k, L, p, store), sorted_flat, N, L, p)
+    vt = gather(pyramid(v, L, p, store), sorted_flat, N, L, p)
     dot = scatter_adjoint(do, sorted_flat, N, L, p)
     dqt, dkt, dvt = attend_adjoint(qt, kt, vt, dot)
     lev, pos = coords_of_flat(sorted_flat, N, L, p)
@@ -439,19 +446,3 @@ def backward_head(q, k, v, do, L: int, p: int, flags: np.ndarray):
             dl[lev[m]][pos[m]] = dt[m]
         grads.append(pool_adjoint(dl, N, p))
     return tuple(grads)
-
-
-# ----------------------------------------------------------------------------
-# [B, H, N, d] wrappers
-# ----------------------------------------------------------------------------
-def forward(q, k, v, L: int, p: int, topk: int, flags=None, out_dtype: str | None = None):
-    """Per-head ``forward_head`` over [B, H, N, d] inputs.  ``flags`` may be a
-    [B, H, |P|] array to inject a selection.  Returns a list (one dict per head,
-    in b-major order)."""
-    B, H = q.shape[:2]
-    outs = []
-    for b in range(B):
-        for h in range(H):
-            fl = None if flags is None else np.asarray(flags[b, h], dtype=bool)
-            outs.append(forward_head(q[b, h], k[b, h], v[b, h], L, p, topk, fl, out_dtype))
-    return outs

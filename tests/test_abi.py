@@ -79,6 +79,29 @@ def test_huge_topk_selects_everything(lh):
     assert st == 0 and S == 1344
 
 
+@pytest.mark.parametrize("topk", [BIG - 1, (1 << 62), (1 << 63) - 1, 1 << 24, (1 << 24) - 1])
+def test_budget_saturates_without_overflow(lh, topk):
+    """(L-1) p k beyond every int64 for a large p: the budget is capped at the
+    candidates without forming the product, so S = |P| (no wrap-around).  At
+    p = 2^24, L = 2, N = 2^24 there are E = 2^24 candidates and one coarsest
+    entry; k = 1 already reaches the cap."""
+    N, p = 1 << 24, 1 << 24
+    st, S, saved, fws, bws = lh.lh_query(1, 1, N, 64, 2, p, topk, "bf16")
+    assert st == 0, lh.lh_last_error()
+    assert S == N + 1
+    assert 0 < saved < (1 << 40) and 0 < fws < (1 << 40) and 0 < bws < (1 << 40)
+
+
+def test_budget_below_the_cap(lh):
+    """Below the cap the budget is exactly (L-1) p k, also for a large p."""
+    N, L, p = 1 << 20, 2, 1 << 10   # E = 2^20 candidates, 2^10 coarsest entries
+    for k in (0, 1, 1023):
+        st, S, *_ = lh.lh_query(1, 1, N, 64, L, p, k, "bf16")
+        assert st == 0 and S == (N >> 10) + (L - 1) * p * k
+    st, S, *_ = lh.lh_query(1, 1, N, 64, L, p, 1024, "bf16")
+    assert st == 0 and S == (N >> 10) + N
+
+
 def test_forward_validation_before_launch(lh):
     """Every one of these fails validation on the host; nothing is enqueued."""
     B, H, N, d, L, p, k = 1, 2, 1024, 64, 3, 4, 64

@@ -8,10 +8,12 @@ Two references, both the fp64 oracle with the GPU's selection injected:
     bf16 MFMA backward takes three operands rounded to bf16 (P, dS and dO~, each
     within the bf16 unit roundoff 2^-8, relative), and consumes the forward's O~
     and LSE, computed from bf16-rounded probabilities;
-  * end to end: the oracle's own fp64 pyramid and backward -- bar 2e-2 of the
+  * end to end: the oracle's own pyramid and backward -- bar 2e-2 of the
     gradient's largest magnitude, the forward's bf16 bar applied to the
-    gradients' scale (pooled rows are stored in bf16, so the logits of pooled
-    entries carry one bf16 rounding).
+    gradients' scale.  In bf16 mode the oracle differentiates its bf16-mode
+    forward (pooled levels stored in bf16, store="bf16"), the forward whose
+    output the forward tests compare; the error against the pure-fp64 pyramid
+    is printed as well.
 At full size, properties that hold at any size: exact scaling by 2,
 run-to-run bit equality, finite values.
 """
@@ -44,7 +46,7 @@ def _grads_stage_consistent(g, do64, N, L, p):
     return out
 
 
-def _run_bwd(lh, cfg, heads, grad_dtype="f32"):
+def _run_bwd(lh, cfg, heads, grad_dtype="f32", pure=True):
     import torch
     say(f"case bwd N={cfg['N']} H={cfg['H']} d={cfg['d']} L={cfg['L']} p={cfg['p']} k={cfg['k']} io={cfg['dtype']}")
     inp = synth.make_inputs(cfg, with_do=True)
@@ -61,12 +63,17 @@ def _run_bwd(lh, cfg, heads, grad_dtype="f32"):
         do64 = synth.as_f64(inp["do"][b, hh], cfg["dtype"])
         got = [bf16_tensor_to_f64(x[b, hh]) for x in (dq, dk, dv)]
         ref_s = _grads_stage_consistent(g, do64, N, L, p)
-        ref_e = orc.backward_head(q64, k64, v64, do64, L, p, g["flags"])
-        for name, a, rs, re in zip(("dq", "dk", "dv"), got, ref_s, ref_e):
+        store = "bf16" if cfg["dtype"] == "bf16" else None
+        ref_e = orc.backward_head(q64, k64, v64, do64, L, p, g["flags"], store=store)
+        ref_p = orc.backward_head(q64, k64, v64, do64, L, p, g["flags"]) if store and pure else None
+        for i, (name, a, rs, re) in enumerate(zip(("dq", "dk", "dv"), got, ref_s, ref_e)):
             scale = np.max(np.abs(re))
             es = np.max(np.abs(a - rs)) / scale
             ee = np.max(np.abs(a - re)) / scale
-            say(f"  head {h} {name}: max|g|={scale:.3e} stage err={es:.3e} end-to-end err={ee:.3e}")
+            msg = f"  head {h} {name}: max|g|={scale:.3e} stage err={es:.3e} end-to-end err={ee:.3e}"
+            if ref_p is not None:
+                msg += f" (pure-fp64 pyramid: {np.max(np.abs(a - ref_p[i])) / scale:.3e})"
+            say(msg)
             extra = 2.0 ** -8 if grad_dtype == "bf16" else 0.0
             assert es <= STAGE_TOL[cfg["dtype"]] + extra
             assert ee <= E2E_TOL + extra
@@ -100,6 +107,16 @@ def test_backward_shapes(lh):
 ], ids=["d64", "p2-L4", "L5", "L6"])
 def test_backward_shapes_bf16(lh, over):
     _run_bwd(lh, synth.config("bwd8k", **over), heads=[0])
+
+
+@pytest.mark.parametrize("L,p,k", [(3, 2, 1536), (5, 4, 1536), (4, 4, 1536)],
+                         ids=["L3-p2-k1536", "L5-p4-k1536", "L4-p4-k1536"])
+def test_backward_ablation_grid_98k(lh, L, p, k):
+    """Backward parity at cells of the pages' ablation grid at the training shape
+    N = 98,304 (one head, d = 128, bf16; S = 30,720, 24,960 and 19,968): the
+    whole head's dQ, dK, dV against the oracle with the GPU's selection injected,
+    stage-consistent and end to end."""
+    _run_bwd(lh, synth.config("98k", H=1, L=L, p=p, k=k), heads=[0], pure=False)
 
 
 def test_backward_properties_scale_and_determinism(lh):
@@ -175,3 +192,30 @@ def test_concurrent_streams(lh):
         assert torch.equal(o.view(torch.int16), ref["o"].view(torch.int16))
         for a, b in zip(g, g_ref):
             assert torch.equal(a, b)
+
+
+def test_autograd_transposed_inputs(lh):
+    """LighthouseAttention through torch.autograd on [B, N, H, d] tensors viewed
+    as [B, H, N, d] (non-contiguous), with a non-contiguous upstream gradient
+    too: the output and the gradients equal those of lh.forward / lh.backward on
+    contiguous copies, bit for bit (the kernels are deterministic)."""
+    import torch
+    cfg = synth.config("bwd8k", N=4096, H=2)
+    inp = synth.make_inputs(cfg, with_do=True)
+    q, k, v, do = (to_dev(inp[n], cfg["dtype"]) for n in ("q", "k", "v", "do"))
+    L, p, topk = cfg["L"], cfg["p"], cfg["k"]
+    o_ref, saved, plan = lh.forward(q, k, v, L, p, topk)
+    g_ref = lh.backward(q, k, v, do, saved, plan)
+    # leaves stored as [B, N, H, d]; the layer sees their [B, H, N, d] transposes
+    base = [x.transpose(1, 2).contiguous().requires_grad_(True) for x in (q, k, v)]
+    views = [b.transpose(1, 2) for b in base]
+    assert not any(x.is_contiguous() for x in views)
+    o = lh.LighthouseAttention.apply(*views, L, p, topk)
+    do_view = do.transpose(1, 2).contiguous().transpose(1, 2)
+    assert not do_view.is_contiguous()
+    o.backward(do_view)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    for b, ref in zip(base, g_ref):
+        assert b.grad.shape == b.shape
+        assert torch.equal(b.grad.transpose(1, 2).contiguous().view(torch.int16), ref.view(torch.int16))

@@ -42,7 +42,8 @@ LSE_TOL = {"f32": 1e-4, "bf16": 1e-3}
 E2E_TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True, sample_rows=256, e2e=True):
+def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True, sample_rows=256, e2e=True,
+               pure=True):
     N, dt = cfg["N"], cfg["dtype"]
     q64, k64, v64 = head_inputs_f64(cfg, inp, h)
     # ---- scores
@@ -91,14 +92,14 @@ def check_head(cfg, inp, g, h, L, p, topk, out_dtype="f32", full_attention=True,
         store = "bf16" if dt == "bf16" else None
         res = orc.forward_head(q64, k64, v64, L, p, topk, store=store)
         nd = int(np.sum(res["flags"] != g["flags"]))
+        say(f"  head {h}: the oracle's own fp64-score selection differs from the GPU's in {nd} entries")
         if nd:
-            say(f"  head {h}: oracle fp64 selection differs from GPU's in {nd} entries; injecting GPU selection")
             res = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"], store=store)
         err = np.max(np.abs(res["o"] - g["o"]))
         msg = f"  head {h}: end-to-end |O - oracle O| = {err:.3e}"
-        if store:
-            pure = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"])
-            msg += f" (pure-fp64 pyramid: {np.max(np.abs(pure['o'] - g['o'])):.3e})"
+        if store and pure:
+            ref = orc.forward_head(q64, k64, v64, L, p, topk, flags=g["flags"])
+            msg += f" (pure-fp64 pyramid: {np.max(np.abs(ref['o'] - g['o'])):.3e})"
         say(msg)
         assert err <= E2E_TOL[dt] + (2.0 ** -8 * np.max(np.abs(res["o"])) if out_dtype == "bf16" else 0.0)
     return S
@@ -229,23 +230,26 @@ def test_topk_dense_boundary_bin(lh, frac, topk, lo, hi):
 
 
 def test_98k_bf16(lh):
-    """98K training shape: every head's selection / order / scatter exact,
-    attention and end-to-end on sampled rows."""
+    """98K training shape (all 8 heads run; three checked): selection, order and
+    scatter exact, attention on sampled rows, and the whole output of each
+    checked head end to end against the oracle's fp64 forward (2e-2 bar), with
+    the size of the oracle's own selection difference printed."""
     cfg = synth.config("98k")
-    _run(lh, cfg, full_attention=False, sample_rows=192, e2e=False, heads=[0, 3, 7])
+    _run(lh, cfg, full_attention=False, sample_rows=192, e2e=True, heads=[0, 3, 7])
 
 
-@pytest.mark.parametrize("L,p,k", [
-    (3, 2, 1536),   # p = 2: pooling fan-in 2, up to 3 contributors per position
-    (5, 2, 2048),   # five levels
-    (4, 4, 3072),
-    (3, 4, 6144),   # the largest k of the pages' grid
+@pytest.mark.parametrize("L,p,k,e2e", [
+    (3, 2, 1536, True),    # p = 2: pooling fan-in 2, up to 3 contributors per position (S = 30,720)
+    (5, 2, 2048, True),    # five levels (S = 22,528)
+    (4, 4, 3072, False),   # S = 38,400
+    (3, 4, 6144, False),   # the largest k of the pages' grid (S = 55,296)
 ])
-def test_ablation_grid_98k_bf16(lh, L, p, k):
+def test_ablation_grid_98k_bf16(lh, L, p, k, e2e):
     """Shapes of the pages' ablation grid at N = 98,304 (one head): selection,
-    order and scatter exact; attention on sampled rows."""
+    order and scatter exact; attention on sampled rows; the whole output end to
+    end where the oracle's forward fits the test's time (S <= 30,720)."""
     cfg = synth.config("98k", H=1, L=L, p=p, k=k)
-    _run(lh, cfg, full_attention=False, sample_rows=128, e2e=False)
+    _run(lh, cfg, full_attention=False, sample_rows=128, e2e=e2e, pure=False)
 
 
 def test_deterministic(lh):

@@ -232,6 +232,12 @@ def _wrap_attend_adjoint_dq_unscaled(orig):
     return attend_adjoint
 
 
+
+def _wrap_backward_ignores_store(orig):
+    def backward_head(q, k, v, do, L, p, flags, store=None):
+        return orig(q, k, v, do, L, p, flags)   # mistake: adjoint at the unrounded rows in bf16 mode
+    return backward_head
+
 MUTATIONS = [
     Mutation("select: ties go to the higher stream index", "select", lambda o: _select_variant(tie_index_desc=True)),
     Mutation("select: budget (L-1) k, factor p dropped", "select", lambda o: _select_variant(budget_without_p=True)),
@@ -254,6 +260,7 @@ MUTATIONS = [
     Mutation("pool adjoint: 1/p^l missing", "pool_adjoint", lambda o: _pool_adjoint_variant(weight=False)),
     Mutation("fixed point: truncation on the way in", "to_fixed", lambda o: _to_fixed_variant(rne=False)),
     Mutation("bf16: truncation instead of rounding", "round_bf16", lambda o: _round_bf16_variant(rne=False)),
+    Mutation("backward: bf16 storage of the pooled levels ignored", "backward_head", _wrap_backward_ignores_store),
 ]
 
 

@@ -418,6 +418,41 @@ def test_backward_finite_differences():
             assert abs(fd - g[t, c]) < 1e-7 * max(1.0, abs(fd)), (which, t, c, fd, g[t, c])
 
 
+def test_backward_bf16_store_finite_differences():
+    """store="bf16": the gradient of the forward whose pooled levels are the
+    exact means plus their bf16 rounding offsets at the base point, held as
+    constants (the storage rounding passes the gradient through), by central
+    differences of that forward built here from the pinned forward steps.  The
+    rounding moves the gradient measurably, so a backward that ignored
+    ``store`` fails."""
+    rng = np.random.default_rng(17)
+    N, d, L, p, k = 32, 4, 3, 2, 2
+    q, kk, v, do = rng.standard_normal((4, N, d))
+    fl = orc.forward_head(q, kk, v, L, p, k, store="bf16")["flags"]
+    dq, dk, dv = orc.backward_head(q, kk, v, do, L, p, fl, store="bf16")
+    offs = [[b - a for a, b in zip(orc.pyramid(x, L, p), orc.pyramid(x, L, p, store="bf16"))]
+            for x in (q, kk, v)]
+    sf = orc.order(fl, N, L, p)
+
+    def loss(*xs):
+        rows = [orc.gather([lv + o for lv, o in zip(orc.pyramid(x, L, p), off)], sf, N, L, p)
+                for x, off in zip(xs, offs)]
+        ot, _ = orc.attend(*rows)
+        return float(np.sum(orc.scatter(ot, sf, N, L, p) * do))
+
+    eps = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        for (t, c) in [(0, 0), (1, 3), (5, 2), (8, 1), (15, 0), (16, 3), (22, 2), (31, 1)]:
+            args_p = [q.copy(), kk.copy(), v.copy()]
+            args_m = [q.copy(), kk.copy(), v.copy()]
+            args_p[which][t, c] += eps
+            args_m[which][t, c] -= eps
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[t, c]) < 1e-7 * max(1.0, abs(fd)), (which, t, c, fd, g[t, c])
+    pure = orc.backward_head(q, kk, v, do, L, p, fl)
+    assert max(np.max(np.abs(a - b)) for a, b in zip(pure, (dq, dk, dv))) > 1e-5
+
+
 def test_backward_L1_textbook():
     """L=1: the gradient is the textbook causal-attention gradient, here by
     plain loops over the softmax Jacobian."""
