@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -49,12 +50,13 @@ void timing_clear() {
 }
 
 // Brackets the launches of one stage with events on the stage's stream while
-// timing is on; does nothing otherwise.  An event that cannot be created or
-// recorded drops that span from the timing (the launches are unaffected).
+// timing is on; does nothing otherwise, or for a negative stage (a call that
+// creates nothing).  An event that cannot be created or recorded drops that
+// span from the timing (the launches are unaffected).
 class Span {
  public:
   Span(int stage, hipStream_t s) : stage_(stage), s_(s) {
-    if (!t_timing) return;
+    if (!t_timing || stage < 0) return;
     if (hipEventCreate(&start_) != hipSuccess) start_ = nullptr;
     else if (hipEventRecord(start_, s_) != hipSuccess) {
       (void)hipEventDestroy(start_);
@@ -361,6 +363,95 @@ lh_status hip_check(hipError_t e, const char *what) {
   return LH_OK;
 }
 
+// Shared checks of the dense attention backward's operands (everything but
+// its workspace).
+lh_status check_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                                   const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
+                                   lh_dtype io) {
+  if (BH < 1 || S < 1) return fail(LH_EINVAL, "BH and S must be >= 1");
+  if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
+  if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
+  if (S * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
+  if (io == LH_BF16 && S % 64 != 0)
+    return fail(LH_EUNSUPPORTED, "LH_BF16 needs S to be a multiple of 64 (got %lld)", (long long)S);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout))
+    return fail(LH_EINVAL, "q, k, v, o, dout must be non-NULL and 16-byte aligned");
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(LH_EINVAL, "dq, dk, dv must be non-NULL and 16-byte aligned");
+  if (!lse || ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be non-NULL and 4-byte aligned");
+  return LH_OK;
+}
+
+// Workspace bytes of the dense attention backward: the (LSE log2 e, delta)
+// pair of every row (LH_BF16) or delta alone (LH_F32).
+size_t attention_backward_ws(int BH, int64_t S, lh_dtype io) {
+  return (io == LH_BF16 ? 8 : 4) * (size_t)BH * (size_t)S;
+}
+
+// The dense attention backward's launches, on validated operands, with its
+// workspace at wsf; `timed`: bracket the stages for stage timing.
+lh_status run_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                                 const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
+                                 lh_dtype io, float *wsf, bool timed, hipStream_t hs) {
+  lh_status st;
+  {
+    Span sp(timed ? LH_STAGE_SCATTER_BWD : -1, timed ? hs : nullptr);   // the row terms take the scatter adjoint's place
+    if ((st = hip_check(lh::launch_attn_rowstats(d, BH, (int)S, dout, io == LH_BF16, o, lse,
+                                                 io == LH_BF16 ? wsf : nullptr, io == LH_BF16 ? nullptr : wsf, hs),
+                        "attention row terms")) != LH_OK)
+      return st;
+  }
+  for (int part = 0; part < 2; ++part) {
+    Span sp(timed ? (part == 0 ? LH_STAGE_ATTN_BWD_DQ : LH_STAGE_ATTN_BWD_DKDV) : -1, timed ? hs : nullptr);
+    hipError_t e;
+    if (io == LH_BF16)
+      e = lh::launch_attn_bwd_mfma(d, BH, (int)S, (int)S, q, k, v, dout, wsf, dq, dk, dv, part, hs);
+    else
+      e = lh::launch_attn_bwd_valu(io, d, BH, (int)S, (int)S, q, k, v, o, lse, reinterpret_cast<const float *>(dout),
+                                   wsf, dq, dk, dv, part, hs);
+    if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
+  }
+  return LH_OK;
+}
+
+}  // namespace
+
+// ---- library-owned scratch of lh_attention_backward_noalloc ----
+// One fixed array per GPU, in the library's code object: the dense attention
+// backward's per-row workspace for callers that cannot allocate.  Host code
+// never uses the name `scratch` as an address (on the host it is only a
+// stand-in for the symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static constexpr size_t kScratchBytes = (size_t)32 << 20;   // 32 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];   // device address of `scratch` per device (null until looked up)
+
+// Device address of `scratch` on the device that runs `hs`.
+lh_status scratch_on(hipStream_t hs, void **out) {
+  int dev = 0, cur = 0;
+  lh_status st;
+  if ((st = hip_check(hipStreamGetDevice(hs, &dev), "hipStreamGetDevice")) != LH_OK) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(LH_EUNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    if ((st = hip_check(hipGetDevice(&cur), "hipGetDevice")) != LH_OK) return st;
+    if (cur != dev && (st = hip_check(hipSetDevice(dev), "hipSetDevice")) != LH_OK) return st;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if ((st = hip_check(e, "hipGetSymbolAddress(scratch)")) != LH_OK) return st;
+    if (!p) return fail(LH_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -562,41 +653,33 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *v, floa
 lh_status lh_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
                                 const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
                                 lh_dtype io, void *ws, size_t ws_bytes, void *stream) {
-  if (BH < 1 || S < 1) return fail(LH_EINVAL, "BH and S must be >= 1");
-  if (d != 64 && d != 128) return fail(LH_EUNSUPPORTED, "head dimension d must be 64 or 128 (got %d)", d);
-  if (io != LH_F32 && io != LH_BF16) return fail(LH_EINVAL, "io dtype must be LH_F32 or LH_BF16");
-  if (S * (int64_t)d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
-  if (io == LH_BF16 && S % 64 != 0)
-    return fail(LH_EUNSUPPORTED, "LH_BF16 needs S to be a multiple of 64 (got %lld)", (long long)S);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout))
-    return fail(LH_EINVAL, "q, k, v, o, dout must be non-NULL and 16-byte aligned");
-  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return fail(LH_EINVAL, "dq, dk, dv must be non-NULL and 16-byte aligned");
-  if (!lse || ((uintptr_t)lse & 3u)) return fail(LH_EINVAL, "lse must be non-NULL and 4-byte aligned");
+  lh_status st = check_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io);
+  if (st != LH_OK) return st;
   if (!aligned16(ws)) return fail(LH_EINVAL, "ws must be non-NULL and 16-byte aligned");
-  const size_t need = (io == LH_BF16 ? 8 : 4) * (size_t)BH * (size_t)S;
+  const size_t need = attention_backward_ws(BH, S, io);
   if (ws_bytes < need) return fail(LH_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return run_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, reinterpret_cast<float *>(ws), true,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
+lh_status lh_attention_backward_noalloc(const void *q, const void *k, const void *v, const float *o,
+                                        const float *lse, const void *dout, float *dq, float *dk, float *dv, int BH,
+                                        int64_t S, int d, lh_dtype io, void *stream) {
+  lh_status st = check_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io);
+  if (st != LH_OK) return st;
+  const size_t need = attention_backward_ws(BH, S, io);
+  if (need > kScratchBytes)
+    return fail(LH_EWORKSPACE,
+                "BH*S = %lld rows need %zu bytes of scratch, beyond the library's fixed %zu bytes "
+                "(at most %zu rows in this dtype); use lh_attention_backward with a workspace",
+                (long long)BH * (long long)S, need, kScratchBytes, kScratchBytes / (io == LH_BF16 ? 8 : 4));
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  float *wsf = reinterpret_cast<float *>(ws);
-  lh_status st;
-  {
-    Span sp(LH_STAGE_SCATTER_BWD, hs);   // the row terms take the place of the scatter adjoint
-    if ((st = hip_check(lh::launch_attn_rowstats(d, BH, (int)S, dout, io == LH_BF16, o, lse,
-                                                 io == LH_BF16 ? wsf : nullptr, io == LH_BF16 ? nullptr : wsf, hs),
-                        "attention row terms")) != LH_OK)
-      return st;
-  }
-  for (int part = 0; part < 2; ++part) {
-    Span sp(part == 0 ? LH_STAGE_ATTN_BWD_DQ : LH_STAGE_ATTN_BWD_DKDV, hs);
-    hipError_t e;
-    if (io == LH_BF16)
-      e = lh::launch_attn_bwd_mfma(d, BH, (int)S, (int)S, q, k, v, dout, wsf, dq, dk, dv, part, hs);
-    else
-      e = lh::launch_attn_bwd_valu(io, d, BH, (int)S, (int)S, q, k, v, o, lse, reinterpret_cast<const float *>(dout),
-                                   wsf, dq, dk, dv, part, hs);
-    if ((st = hip_check(e, "attention backward")) != LH_OK) return st;
-  }
-  return LH_OK;
+  void *sp = nullptr;
+  if ((st = scratch_on(hs, &sp)) != LH_OK) return st;
+  // every row of the scratch that the backward reads is written by its first
+  // kernel in the same call, so nothing needs clearing
+  return run_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, reinterpret_cast<float *>(sp), false,
+                                hs);
 }
 
 lh_status lh_layer_query(int B, int H, int64_t N, int d_model, int d, int L, int p, int64_t topk, lh_dtype io,

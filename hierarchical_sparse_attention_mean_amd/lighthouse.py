@@ -63,6 +63,8 @@ _lib.lh_attention_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i,
 _lib.lh_attention_forward.restype = _i
 _lib.lh_attention_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp, _sz, _vp]
 _lib.lh_attention_backward.restype = _i
+_lib.lh_attention_backward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i, _i, _vp]
+_lib.lh_attention_backward_noalloc.restype = _i
 _lib.lh_layer_query.argtypes = [_i, _i, _i64, _i, _i, _i, _i, _i64, _i, _P(_i64), _P(_sz), _P(_sz), _P(_sz)]
 _lib.lh_layer_query.restype = _i
 _lib.lh_layer_saved_layout.argtypes = [_i, _i, _i64, _i, _i, _i, _i, _i64, _i, _P(LayerLayout)]
@@ -188,6 +190,11 @@ def lh_attention_backward(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, ws, w
     return _lib.lh_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                       _ptr(dk), _ptr(dv), BH, S, d, dtype_code(io), _ptr(ws), ws_bytes,
                                       _stream(stream))
+
+
+def lh_attention_backward_noalloc(q, k, v, o, lse, dout, dq, dk, dv, BH, S, d, io, stream=None):
+    return _lib.lh_attention_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), BH, S, d, dtype_code(io), _stream(stream))
 
 
 def lh_layer_query(B, H, N, d_model, d, L, p, topk, io):

@@ -33,9 +33,12 @@
  *  - Supported: d in {64, 128}; io dtype LH_F32 or LH_BF16 (bf16 storage, fp32
  *    arithmetic, bf16 MFMA for the attention); L >= 1; p >= 2; topk >= 0.
  *    topk larger than the candidates selects everything (S = |P|).
- *  - No global mutable state except the thread-local error text and the
- *    thread-local stage timing switch (lh_timing_begin): calls are re-entrant;
- *    concurrent calls on different streams must use distinct buffers.
+ *  - No global mutable state except the thread-local error text, the
+ *    thread-local stage timing switch (lh_timing_begin), and the fixed scratch
+ *    array of lh_attention_backward_noalloc (with its per-GPU address, looked up
+ *    once): calls are re-entrant; concurrent calls on different streams must use
+ *    distinct buffers (and lh_attention_backward_noalloc calls on one GPU must
+ *    not overlap).
  */
 #ifndef LIGHTHOUSE_H
 #define LIGHTHOUSE_H
@@ -145,6 +148,25 @@ lh_status lh_attention_forward(const void *q, const void *k, const void *v, floa
 lh_status lh_attention_backward(const void *q, const void *k, const void *v, const float *o, const float *lse,
                                 const void *dout, float *dq, float *dk, float *dv, int BH, int64_t S, int d,
                                 lh_dtype io, void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * computation and kernels as lh_attention_backward (bit-identical results), but
+ * with no workspace argument.  Its per-row scratch lives in a fixed array inside
+ * the library (32 MiB per GPU, held from when the library is loaded until the
+ * process ends), which bounds the rows: BH * S <= 4,194,304 in LH_BF16 (8 bytes
+ * per row) or 8,388,608 in LH_F32 (4 bytes per row); larger shapes return
+ * LH_EWORKSPACE before anything is enqueued.  The call allocates and frees
+ * nothing; on its first use on a GPU it looks up that GPU's copy of the array
+ * (hipGetSymbolAddress) and keeps the address.  Nothing in the array needs to
+ * start at zero: the call writes every row it reads.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  Stage timing
+ * records nothing for this call.  Other arguments and errors as
+ * lh_attention_backward. */
+lh_status lh_attention_backward_noalloc(const void *q, const void *k, const void *v, const float *o,
+                                        const float *lse, const void *dout, float *dq, float *dk, float *dv, int BH,
+                                        int64_t S, int d, lh_dtype io, void *stream);
 
 /* ---- Projection-inclusive layer ----
  * The attention layer of the decoder the pages train, around the Lighthouse

@@ -223,3 +223,19 @@ def test_binding_refuses_host_tensors(lh):
     w = torch.zeros((128, 128))
     with pytest.raises(ValueError, match="device"):
         lh.layer_forward(x, w, w, w, w, 2, 3, 4, 64)
+
+
+def test_noalloc_backward_refuses_beyond_its_array(lh):
+    """The no-allocation dense backward bounds its rows by its fixed array
+    (8 bytes per row in bf16, 4 in fp32, 32 MiB): larger shapes fail validation
+    on the host, before any device call."""
+    fake = 1 << 20                     # aligned, never dereferenced
+    args = [fake] * 9
+    limit_bf16, limit_f32 = (32 << 20) // 8, (32 << 20) // 4
+    assert lh.lh_attention_backward_noalloc(*args, 8, limit_bf16 // 8 + 64, 128, "bf16") == 4
+    assert "scratch" in lh.lh_last_error()
+    assert lh.lh_attention_backward_noalloc(*args, 1, limit_f32 + 1, 64, "f32") == 4
+    # other validation as the workspace variant: S not a multiple of 64 in bf16, bad d, null pointers
+    assert lh.lh_attention_backward_noalloc(*args, 1, 100, 128, "bf16") == 3
+    assert lh.lh_attention_backward_noalloc(*args, 1, 128, 96, "bf16") == 3
+    assert lh.lh_attention_backward_noalloc(None, *args[1:], 1, 128, 128, "bf16") == 1
