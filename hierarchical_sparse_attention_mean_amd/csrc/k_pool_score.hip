@@ -6,8 +6,10 @@
 //   Sec. 3.4  level-0 scores are the per-head l2 norms ||Q_t|| (query score QK)
 //             and ||K_t|| (key score KQ); coarser levels take the max of the
 //             level-0 scores over their window.
-// It also records, per head, the range of the candidates' score bits (levels
-// 0..L-2, both streams) for the top-k histogram.
+// For the top-k that follows it also records, per work-group, the range of the
+// candidates' score bits it produced (levels 0..L-2), and its V plane clears the
+// top-k's per-head state and histogram (nothing else touches them before the
+// top-k's first pass, which starts after this kernel has finished).
 //
 // Work mapping: grid plane z = 0, 1, 2 pools Q, K, V respectively; the Q and K
 // planes also compute the query and key scores.  A work-group of 256 threads
@@ -124,6 +126,12 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   const T *x = z == 0 ? q : (z == 1 ? k : v);
   const long long hoff = (long long)h * s.N * D;
   float *sc = scores + (long long)h * 2 * s.P + (z == 1 ? s.P : 0);   // QK or KQ stream
+  if (z == 2) {   // clear head h's top-k state and histogram, spread over the plane's work-groups
+    unsigned int *hh = reinterpret_cast<unsigned int *>(ws + w.hist) + (long long)h * kHistBins;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < kHistBins; i += gridDim.x * 256) hh[i] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < (int)(sizeof(TopkState) / 4))
+      reinterpret_cast<unsigned int *>(reinterpret_cast<TopkState *>(ws + w.state) + h)[threadIdx.x] = 0u;
+  }
 
   // running window sums and max-pooled scores per level l >= 1 (ML >= L levels)
   float acc[ML][EL], mx[ML];
@@ -211,41 +219,29 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
     for (int u = 0; u < NB; ++u) cur[u] = nxt[u];
   }
   if (L == 1 || !scored) return;
-  // range of the candidates' score bits over both streams (a key's upper half is
-  // the larger of its two scores, so this range contains every key's), for the
-  // top-k histogram
-  __shared__ unsigned int red_min[256], red_max[256];
-  red_min[threadIdx.x] = umin;
-  red_max[threadIdx.x] = umax;
+  // range of this work-group's candidate score bits (min > max if it has none);
+  // the union over both streams' work-groups contains every key's upper half,
+  // the larger of its two scores
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    umin = min(umin, (unsigned int)__shfl_xor((int)umin, m));
+    umax = max(umax, (unsigned int)__shfl_xor((int)umax, m));
+  }
+  __shared__ unsigned int red_min[4], red_max[4];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_min[wv] = umin;
+    red_max[wv] = umax;
+  }
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (threadIdx.x < st) {
-      red_min[threadIdx.x] = min(red_min[threadIdx.x], red_min[threadIdx.x + st]);
-      red_max[threadIdx.x] = max(red_max[threadIdx.x], red_max[threadIdx.x + st]);
-    }
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int mn = min(min(red_min[0], red_min[1]), min(red_min[2], red_min[3]));
+    const unsigned int mxv = max(max(red_max[0], red_max[1]), max(red_max[2], red_max[3]));
+    reinterpret_cast<uint2 *>(ws + w.brange)[((long long)h * 2 + z) * s.npool + blockIdx.x] = make_uint2(mn, mxv);
   }
-  if (threadIdx.x == 0 && red_min[0] <= red_max[0]) {
-    TopkState *stt = reinterpret_cast<TopkState *>(ws + w.state) + h;
-    atomicMin(&stt->umin, red_min[0]);
-    atomicMax(&stt->umax, red_max[0]);
-  }
-}
-
-__global__ void k_fill_u32(unsigned int *p, size_t n, unsigned int value) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = value;
 }
 
 }  // namespace
-
-hipError_t launch_fill_u32(void *p, size_t n_u32, unsigned int value, hipStream_t st) {
-  if (n_u32 == 0) return hipSuccess;
-  size_t blocks = (n_u32 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(reinterpret_cast<unsigned int *>(p), n_u32, value);
-  return hipGetLastError();
-}
 
 template <typename T, int D>
 static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *k, const void *v, char *ws,
@@ -264,10 +260,7 @@ static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                              const FwdWs &w, float *scores, hipStream_t st) {
   if (s.L > kMaxL) return hipErrorInvalidValue;
-  const int CH = s.d / (s.L <= 4 ? 8 : 4);   // elements per lane as in the kernel (ML <= 3: 8)
-  const int RG = 256 / CH;
-  const int nwin = s.n[s.L - 1];
-  dim3 grid((nwin + RG - 1) / RG, s.BH, 3);   // one plane per tensor: Q, K, V
+  dim3 grid(s.npool, s.BH, 3);   // one plane per tensor: Q, K, V; s.npool = coarsest windows / row-groups
   char *wsb = reinterpret_cast<char *>(ws);
   if (s.io == LH_BF16) {
     if (s.d == 128) pool_score_ml<uint16_t, 128>(s, grid, q, k, v, wsb, w, scores, st);

@@ -153,6 +153,8 @@ lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
   s->Sv = (s->S + 63) & ~63;
   if ((int64_t)s->S * d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
   s->ntile = (s->N + lh::kCompactTile - 1) / lh::kCompactTile;
+  const int rg = lh::pool_score_rowgroups(d, L);
+  s->npool = (s->n[L - 1] + rg - 1) / rg;
   return LH_OK;
 }
 
@@ -194,11 +196,13 @@ void fwd_ws_layout(const lh::Shape &s, lh::FwdWs *w) {
   memset(w, 0, sizeof *w);
   for (int l = 1; l < s.L; ++l)
     for (int t = 0; t < 3; ++t) w->lev[l][t] = take(es * BH * (size_t)s.n[l] * d);
-  // state and histogram are adjacent: one fill kernel clears both
+  w->brange = take(8 * BH * 2 * (size_t)s.npool);
   w->state = take(sizeof(lh::TopkState) * BH);
-  w->hist = cur;
-  cur = align_up(cur + 4 * BH * lh::kHistBins);
-  w->cand = take(8 * BH * (size_t)s.E);
+  w->hist = take(4 * BH * lh::kHistBins);
+  const int nbf = lh::topk_blocks(s.P, lh::kFilterBlocks);
+  w->cstride = (long long)nbf * lh::topk_chunk(s.P, nbf);
+  w->cand = take(8 * BH * (size_t)w->cstride);
+  w->ccount = take(4 * BH * (size_t)lh::kFilterBlocks);
   w->tilecount = take(4 * BH * (size_t)s.ntile);
   w->total = cur;
 }
@@ -525,12 +529,8 @@ lh_status lh_forward(const void *q, const void *k, const void *v, void *o, lh_dt
   float *ot = reinterpret_cast<float *>(sv + sl.ot);
   float *lse = reinterpret_cast<float *>(sv + sl.lse);
 
-  // (ii) top-k state (umin = ~0, the rest 0) and histogram cleared by a kernel
-  {
-    Span sp(LH_STAGE_TOPK, hs);
-    if ((st = hip_check(lh::launch_topk_init(s, ws, fw, hs), "topk_init")) != LH_OK) return st;
-  }
-  // (i)+(ii) pyramid and scores in one pass over Q, K, V
+  // (i)+(ii) pyramid and scores in one pass over Q, K, V (which also clears the
+  // top-k state and histogram and records each work-group's score range)
   {
     Span sp(LH_STAGE_POOL_SCORE, hs);
     if ((st = hip_check(lh::launch_pool_score(s, q, k, v, ws, fw, scores, hs), "pool_score")) != LH_OK) return st;

@@ -30,29 +30,55 @@ struct Shape {
   int S;                     // gathered length per head
   int Sv;                    // row stride of the transposed copies: S rounded up to a multiple of 64
   int ntile;                 // compaction tiles per head
+  int npool;                 // pool+score work-groups per head and tensor (coarsest windows / row-groups)
 };
+
+// Row-groups (coarsest windows) per pool+score work-group of 256 threads: a row
+// of d elements is spread over d / EL lanes, EL = 8 up to four levels, 4 beyond.
+__host__ __device__ inline int pool_score_rowgroups(int d, int L) { return 256 / (d / (L <= 4 ? 8 : 4)); }
 
 constexpr int kCompactTile = 1024;   // base positions per compaction work-group
 constexpr int kHistBins = 4096;      // first radix-select digit of the top-k
-constexpr int kTopkCandLds = 8192;   // candidates sorted in LDS by the bitonic stage
 
-// Per-head state of the top-k (in the forward workspace).
+// Work split of the top-k's histogram and filter passes over n entries of a
+// head: up to maxb work-groups (kHistBlocks, kFilterBlocks) of kTopkThreads
+// threads, each taking an equal chunk (a whole number of work-group widths) in
+// rounds of kTopkRound entries per thread.
+constexpr int kTopkThreads = 1024;
+constexpr int kHistBlocks = 32;     // few work-groups: each merges its histogram with global atomics
+constexpr int kFilterBlocks = 64;   // two per compute unit at 8 heads
+constexpr int kTopkRound = 8;
+__host__ __device__ inline int topk_blocks(long long n, int maxb) {
+  const long long r = (long long)kTopkRound * kTopkThreads;
+  const long long b = (n + r - 1) / r;
+  return (int)(b < 1 ? 1 : (b > maxb ? maxb : b));
+}
+__host__ __device__ inline long long topk_chunk(long long n, int nb) {
+  return ((n + nb - 1) / nb + kTopkThreads - 1) / kTopkThreads * kTopkThreads;
+}
+
+// Per-head state of the top-k (in the forward workspace).  The pool+score
+// kernel clears it (and the histogram); the histogram pass writes the score
+// range, the filter pass the boundary bin and `need`.
 struct TopkState {
   unsigned int umin;        // min over candidates of the score bits (upper key half)
   unsigned int umax;        // max of the same
-  unsigned int cand_count;  // keys in the boundary histogram bin
   unsigned int bstar;       // boundary bin
+  unsigned int pad0;
   long long need;           // keys still to take from the boundary bin
-  long long pad;
+  long long pad1;
 };
 
 // Forward workspace layout (byte offsets).
 struct FwdWs {
   size_t lev[LH_MAX_LEVELS][3];  // pooled Q, K, V of level l >= 1 ([BH][n_l][d], io dtype)
+  size_t brange;                 // uint2 [BH][2][npool]: (min, max) of each pool+score work-group's candidate score bits
   size_t state;                  // TopkState [BH]
   size_t hist;                   // uint32 [BH][kHistBins]
-  size_t cand;                   // uint64 [BH][E]
+  size_t cand;                   // uint64 [BH][cstride]: boundary-bin keys, filter work-group b's at b * chunk
+  size_t ccount;                 // uint32 [BH][kFilterBlocks]: keys each filter work-group wrote
   size_t tilecount;              // int32 [BH][ntile]
+  long long cstride;             // candidate slots per head: filter work-groups x chunk (>= P)
   size_t total;
 };
 
@@ -123,10 +149,8 @@ __device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f
 }
 
 // ---- launchers (each enqueues on `st`, returns hipGetLastError()) ----
-hipError_t launch_fill_u32(void *p, size_t n_u32, unsigned int value, hipStream_t st);
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,
                              const FwdWs &w, float *scores, hipStream_t st);
-hipError_t launch_topk_init(const Shape &s, void *ws, const FwdWs &w, hipStream_t st);
 hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, const float *scores, uint8_t *flags,
                        hipStream_t st);
 hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, const void *v, void *ws,

@@ -222,7 +222,7 @@ lh_status lh_layer_backward(const void *x, const void *wq, const void *wk, const
 /* Stages of lh_forward / lh_backward (and of the layer entry points), for stage timing. */
 typedef enum {
   LH_STAGE_POOL_SCORE = 0,   /* (i)+(ii): pyramid and scores, one pass over Q, K, V          */
-  LH_STAGE_TOPK = 1,         /* (ii): joint top-B selection (state clear + 3 passes)          */
+  LH_STAGE_TOPK = 1,         /* (ii): joint top-B selection (histogram, filter, refine passes) */
   LH_STAGE_GATHER = 2,       /* (iii): topological compaction and gather                      */
   LH_STAGE_ATTN_FWD = 3,     /* (iii): causal attention over the sub-sequence (Eq. 9)         */
   LH_STAGE_SCATTER = 4,      /* (iv): scatter to the base positions                           */

@@ -202,20 +202,22 @@ def _boundary_candidates(qk_flat, kq_flat, N, L, p, topk):
     return int(hist[b])
 
 
-@pytest.mark.parametrize("frac,topk,lo,hi", [
-    (0.01, 16, 1, 1024),          # one key per thread
-    (0.05, 128, 1025, 2048),      # two
-    (0.10, 256, 2049, 4096),      # four
-    (0.20, 256, 4097, 8192),      # eight
-    (0.50, 256, 8193, 1 << 30),   # more than LDS holds: radix passes over the list
+@pytest.mark.parametrize("N,frac,topk,lo,hi", [
+    (16384, 0.01, 16, 1, 1024),
+    (16384, 0.05, 128, 1025, 2048),
+    (16384, 0.10, 256, 2049, 4096),
+    (16384, 0.20, 256, 4097, 8192),
+    (16384, 0.50, 256, 8193, 16384),        # up to the most candidates ranked in LDS
+    (65536, 0.50, 256, 16385, 1 << 30),     # more than LDS holds: radix passes over the list
 ])
-def test_topk_dense_boundary_bin(lh, frac, topk, lo, hi):
+def test_topk_dense_boundary_bin(lh, N, frac, topk, lo, hi):
     """Scores with two values only: Q_t = c_t u with c_t in {1, 2} (a seeded
     fraction `frac` of rows get 2), K_t = u / 4, so every key's score is |u| or
     2|u| exactly and the boundary bin holds every entry scoring 2|u|.  Its size
-    (checked from the GPU's scores) steers the refine through each of its sort
-    sizes and the radix path; the selection must still be bit-exact."""
-    cfg = synth.config("tiny", N=16384, H=1, k=topk)
+    (checked from the GPU's scores) steers the refine through candidate lists
+    of every size its LDS ranking takes, and past them into the radix path; the
+    selection must still be bit-exact."""
+    cfg = synth.config("tiny", N=N, H=1, k=topk)
     inp = synth.make_inputs(cfg)
     u = (np.linspace(0.5, 1.5, cfg["d"]) / 8).astype(np.float32)
     c = np.where(np.random.default_rng(7).random(cfg["N"]) < frac, 2.0, 1.0).astype(np.float32)
