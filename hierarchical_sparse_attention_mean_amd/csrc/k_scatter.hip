@@ -365,6 +365,205 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(Shape s, const void *__rest
   }
 }
 
+constexpr int kWalkCoarse = 2;   // most levels k_scatter_bwd_walk combines through LDS
+
+// Position-major scatter adjoint, when p = 2^LG is 2 or 4 and the coarsest
+// range p^(L-1) fits a work-group's span W = RG GW.  In u = t + 1 the range of
+// entry (l, i) is the aligned block [(i+1) p^l, (i+2) p^l), so a walk over u
+// in aligned blocks meets every entry's range exactly once, like the pooling
+// walk of the forward: row group g of the work-group (C8 lanes, 8 columns
+// each) reads the dO rows of its GW = p^A consecutive positions once (in
+// batches of NB), sums the ranges of levels 0 .. A in registers (level l's sum
+// is the sum of its p children's, levels ascending), and on completing the
+// range of a selected entry writes its dO~ row and delta; the work-group then
+// forms the ranges of levels A+1 .. L-1 from its row groups' block sums through
+// LDS, in row-group order.  dO is read once (k_scatter_bwd reads a row once per
+// selected entry covering it, up to L times).  One extra work-group per head
+// writes the zero padding rows (bf16 mode).
+template <int D, bool BF16, int GW, int LG>
+__global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, int nwg, const void *__restrict__ dout,
+                                                          int dout_dtype, const int *__restrict__ slot,
+                                                          const float *__restrict__ ot, float *__restrict__ dot32,
+                                                          uint16_t *__restrict__ dotb, float *__restrict__ delta,
+                                                          const float *__restrict__ lse, float *__restrict__ rows) {
+  constexpr int C8 = D / 8;
+  constexpr int RG = 256 / C8;
+  constexpr int W = RG * GW;           // u positions per work-group
+  constexpr int NB = GW < 8 ? GW : 8;  // rows per batch
+  constexpr int A = __builtin_ctz(GW) / LG;   // levels 1 .. A summed in registers (p^A = GW)
+  static_assert((1 << (A * LG)) == GW, "GW is a power of p");
+  // slots of the block's entries of levels 1 .. A: level l has GW >> (l LG) of them, at sbase(l)
+  constexpr auto sbase = [](int l) {
+    int o = 0;
+    for (int k = 1; k < l; ++k) o += GW >> (k * LG);
+    return o;
+  };
+  constexpr int NSL = sbase(A + 1) > 0 ? sbase(A + 1) : 1;
+  __shared__ float part[RG][D + 4];
+  const int h = blockIdx.y;
+  const int c = threadIdx.x % C8, g = threadIdx.x / C8;
+  if (blockIdx.x == nwg) {   // bf16 mode: zero padding rows S .. Sv-1
+    if constexpr (BF16) {
+      for (int r = s.S + g; r < s.Sv; r += RG) {
+        *reinterpret_cast<uint4 *>(dotb + ((long long)h * s.Sv + r) * D + c * 8) = make_uint4(0u, 0u, 0u, 0u);
+        if (c == 0) *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + r)) = make_float2(0.f, 0.f);
+      }
+    }
+    return;
+  }
+  const int *sl = slot + (long long)h * s.P;
+  const int ub = blockIdx.x * W + g * GW;   // first u of this row group's block
+  const long long dbase = ((long long)h * s.N) * D + c * 8;
+
+  // Output of entry slot m with range sum x (dO~ as the attention backward
+  // reads it, and delta = rowsum(dO~ o O~)); uniform over the row group.
+  auto emit_o = [&](int m, const float (&x)[8], const float (&o8)[8]) {
+    float y[8];
+    uint16_t hb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = x[e];
+      if constexpr (BF16) {
+        hb[e] = f32_to_bf16_rne(y[e]);
+        y[e] = bf16_to_f32(hb[e]);
+      }
+    }
+    float dl = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dl = fmaf(y[e], o8[e], dl);
+#pragma unroll
+    for (int xo = 1; xo < C8; xo <<= 1) dl += __shfl_xor(dl, xo);
+    if constexpr (BF16) {
+      uint4 w;
+      w.x = (unsigned)hb[0] | ((unsigned)hb[1] << 16);
+      w.y = (unsigned)hb[2] | ((unsigned)hb[3] << 16);
+      w.z = (unsigned)hb[4] | ((unsigned)hb[5] << 16);
+      w.w = (unsigned)hb[6] | ((unsigned)hb[7] << 16);
+      *reinterpret_cast<uint4 *>(dotb + ((long long)h * s.Sv + m) * D + c * 8) = w;
+      if (c == 0)
+        *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + m)) =
+            make_float2(lse[(long long)h * s.S + m] * 1.4426950408889634f, dl);
+    } else {
+      if (c == 0) delta[(long long)h * s.S + m] = dl;
+      float *dst = dot32 + ((long long)h * s.S + m) * D + c * 8;
+      *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4 *>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  };
+  auto emit = [&](int m, const float (&x)[8]) {
+    float o8[8];
+    load_row8(ot + ((long long)h * s.S + m) * D + c * 8, o8);
+    emit_o(m, x, o8);
+  };
+  // slot of the entry of level l whose range ends at u, or -1
+  auto slot_at = [&](int l, int u) {
+    const int i = (u >> (l * LG)) - 1;
+    return (i >= 0 && i < s.n[l]) ? sl[s.off[l] + i] : -1;
+  };
+
+  int msl[NSL];
+#pragma unroll
+  for (int l = 1; l <= A; ++l)
+#pragma unroll
+    for (int k = 0; k < (GW >> (l * LG)); ++k) msl[sbase(l) + k] = slot_at(l, ub + ((k + 1) << (l * LG)) - 1);
+  // the entries of levels A+1 .. L-1 whose range this row group combines (see
+  // below) and their O~ rows, loaded ahead of the walk
+  constexpr int NCO = kWalkCoarse;   // levels above A (the launcher dispatches L - 1 - A <= kWalkCoarse)
+  int mco[NCO];
+  float oco[NCO][8];
+#pragma unroll
+  for (int j = 0; j < NCO; ++j) {
+    const int l = A + 1 + j;
+    mco[j] = -1;
+    if (l < s.L && g < W / s.pw[l]) {
+      mco[j] = slot_at(l, blockIdx.x * W + (g + 1) * s.pw[l] - 1);
+      if (mco[j] >= 0) load_row8(ot + ((long long)h * s.S + mco[j]) * D + c * 8, oco[j]);
+    }
+  }
+  float acc[A + 1][8];   // acc[l]: running range sum of level l >= 1; acc[0]: the block sum
+#pragma unroll
+  for (int l = 0; l <= A; ++l)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+#pragma unroll
+  for (int r0 = 0; r0 < GW; r0 += NB) {
+    // a batch of NB rows (zeros outside 0 <= t < N) and their level-0 slots
+    uint4 raw[NB];
+    float xf[BF16 ? 1 : NB][8];
+    int m0[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int t = ub + r0 + r - 1;
+      const bool ok = t >= 0 && t < s.N;
+      m0[r] = ok ? sl[t] : -1;
+      if constexpr (BF16) {
+        raw[r] = ok ? *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(dout) + dbase +
+                                                       (long long)t * D)
+                    : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        if (ok) load_row8(reinterpret_cast<const float *>(dout) + dbase + (long long)t * D, xf[r]);
+        else
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xf[r][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int rr = r0 + r;
+      float x[8];
+      if constexpr (BF16) {
+        const unsigned v[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(v[e] << 16);
+          x[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = xf[r][e];
+      }
+      if (m0[r] >= 0) emit(m0[r], x);   // level 0: the row itself
+      if constexpr (A == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[0][e] = x[e];   // the block sum (GW = 1)
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[1][e] += x[e];
+#pragma unroll
+        for (int l = 1; l <= A; ++l) {
+          if (((rr + 1) & ((1 << (l * LG)) - 1)) != 0) break;   // range of level l not complete
+          const int m = msl[sbase(l) + (rr >> (l * LG))];
+          if (m >= 0) emit(m, acc[l]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (l < A) acc[l + 1][e] += acc[l][e];
+            else acc[0][e] = acc[l][e];   // the block sum (level A)
+            acc[l][e] = 0.f;
+          }
+        }
+      }
+    }
+  }
+  if (A + 1 >= s.L) return;   // every level handled in registers
+  // levels A+1 .. L-1: sums of consecutive row groups' block sums, in order
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][c * 8 + e] = acc[0][e];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NCO; ++j) {
+    if (mco[j] < 0) continue;   // no such level, range or selection
+    const int per = s.pw[A + 1 + j] / GW;   // row groups per range of the level
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = part[g * per][c * 8 + e];
+      for (int r = 1; r < per; ++r) v += part[g * per + r][c * 8 + e];
+      x[e] = v;
+    }
+    emit_o(mco[j], x, oco[j]);
+  }
+}
+
 // One thread per 8 consecutive elements of a position's row of dQ, dK, dV
 // (16-byte stores); slots of the position's entries looked up first.
 // Arithmetic: per level in ascending order, acc = fma(dX~, 1/p^l, acc).
@@ -496,13 +695,52 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
-                              const float *lse, float *dot32, uint16_t *dotb, float *delta, float *rows,
-                              hipStream_t st) {
+hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *slot, const int *coords,
+                              const float *ot, const float *lse, float *dot32, uint16_t *dotb, float *delta,
+                              float *rows, hipStream_t st) {
+  const bool bf = s.io == LH_BF16;
+  // position-major walk: four or more levels (where k_scatter_bwd's re-reads of
+  // dO dominate), p = 2 or 4, and the coarsest range fits a work-group's span
+  if ((s.p == 2 || s.p == 4) && s.L >= 4) {
+    int gw = 1, a = 0;   // rows per row group: the largest p^a <= 16 with a <= L - 1
+    while (a + 1 < s.L && gw * s.p <= 16) {
+      gw *= s.p;
+      ++a;
+    }
+    const int rg = 256 / (s.d / 8);
+    const long long span = (long long)rg * gw;
+    if (gw > 1 && s.pw[s.L - 1] <= span && s.L - 1 - a <= kWalkCoarse) {
+      const int nwg = (int)((s.N + 1 + span - 1) / span);
+      dim3 grid((unsigned)(nwg + 1), s.BH);
+#define LH_SW(D, B, G, LG) \
+  k_scatter_bwd_walk<D, B, G, LG><<<grid, 256, 0, st>>>(s, nwg, dout, dout_dtype, slot, ot, dot32, dotb, delta, lse, rows)
+#define LH_SWG(D, B)                          \
+  do {                                        \
+    if (s.p == 4) {                           \
+      if (gw == 16) LH_SW(D, B, 16, 2);       \
+      else LH_SW(D, B, 4, 2);                 \
+    } else {                                  \
+      if (gw == 16) LH_SW(D, B, 16, 1);       \
+      else if (gw == 8) LH_SW(D, B, 8, 1);    \
+      else if (gw == 4) LH_SW(D, B, 4, 1);    \
+      else LH_SW(D, B, 2, 1);                 \
+    }                                         \
+  } while (0)
+      if (s.d == 128) {
+        if (bf) LH_SWG(128, true);
+        else LH_SWG(128, false);
+      } else {
+        if (bf) LH_SWG(64, true);
+        else LH_SWG(64, false);
+      }
+#undef LH_SWG
+#undef LH_SW
+      return hipGetLastError();
+    }
+  }
   // bf16 mode also writes the zero padding rows / columns up to Sv (a multiple of 64)
   const int spb = 256 / (s.d / 8);
   dim3 grid((unsigned)(((s.io == LH_BF16 ? s.Sv : s.S) + spb - 1) / spb), s.BH);
-  const bool bf = s.io == LH_BF16;
 #define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, delta, lse, rows)
   if (s.d == 128) {
     if (bf) LH_SB(128, true);

@@ -52,12 +52,17 @@ void timing_clear() {
 // Brackets the launches of one stage with events on the stage's stream while
 // timing is on; does nothing otherwise, or for a negative stage (a call that
 // creates nothing).  An event that cannot be created or recorded drops that
-// span from the timing (the launches are unaffected).
+// span from the timing (the launches are unaffected).  The events only time:
+// they are created without the system-scope fence (cache writeback and
+// invalidation) that a default event performs when recorded, which would
+// otherwise stall the next stage's first launch by microseconds.
+hipError_t timing_event(hipEvent_t *e) { return hipEventCreateWithFlags(e, hipEventDisableSystemFence); }
+
 class Span {
  public:
   Span(int stage, hipStream_t s) : stage_(stage), s_(s) {
     if (!t_timing || stage < 0) return;
-    if (hipEventCreate(&start_) != hipSuccess) start_ = nullptr;
+    if (timing_event(&start_) != hipSuccess) start_ = nullptr;
     else if (hipEventRecord(start_, s_) != hipSuccess) {
       (void)hipEventDestroy(start_);
       start_ = nullptr;
@@ -66,7 +71,7 @@ class Span {
   ~Span() {
     if (!start_) return;
     hipEvent_t stop;
-    if (hipEventCreate(&stop) != hipSuccess) {
+    if (timing_event(&stop) != hipSuccess) {
       (void)hipEventDestroy(start_);
       return;
     }
@@ -604,11 +609,10 @@ lh_status lh_backward(const void *q, const void *k, const void *v, const void *d
   (void)q;
   (void)k;
   (void)v;
-  (void)slot;
   // adjoint of the scatter: dO~ (and delta = rowsum(dO~ * O~))
   {
     Span sp(LH_STAGE_SCATTER_BWD, hs);
-    if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, coords, ot, lse, dot, dotb, delta, rows, hs),
+    if ((st = hip_check(lh::launch_scatter_bwd(s, dout, dout_dtype, slot, coords, ot, lse, dot, dotb, delta, rows, hs),
                         "scatter_bwd")) != LH_OK)
       return st;
   }

@@ -158,9 +158,9 @@ hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, c
                                  void *qt, void *kt, void *vt, hipStream_t st);
 hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, const float *ot, void *o,
                           int o_dtype, hipStream_t st);
-hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *coords, const float *ot,
-                              const float *lse, float *dot32, uint16_t *dotb, float *delta, float *rows,
-                              hipStream_t st);
+hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, const int *slot, const int *coords,
+                              const float *ot, const float *lse, float *dot32, uint16_t *dotb, float *delta,
+                              float *rows, hipStream_t st);
 hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, const float *dkt,
                            const float *dvt, void *dq, void *dk, void *dv, int grad_dtype, hipStream_t st);
 // akm / bkm: A / B k-major (view (r, c) = (m, k) / (n, k)), else mn-major ((k, m) / (k, n)).
