@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void k_attn_rowstats(int S, const void *__rest
 hipError_t launch_attn_rowstats(int d, int BH, int S, const void *dout, int dout_bf16, const float *o,
                                 const float *lse, float *pairs, float *delta, hipStream_t st) {
   dim3 grid((unsigned)((S + 63) / 64), BH);
-  if (d == 128) k_attn_rowstats<128><<<grid, 256, 0, st>>>(S, dout, dout_bf16, o, lse, pairs, delta);
-  else k_attn_rowstats<64><<<grid, 256, 0, st>>>(S, dout, dout_bf16, o, lse, pairs, delta);
+  if (d == 128) lh::launch(k_attn_rowstats<128>, grid, 256, 0, st, S, dout, dout_bf16, o, lse, pairs, delta);
+  else lh::launch(k_attn_rowstats<64>, grid, 256, 0, st, S, dout, dout_bf16, o, lse, pairs, delta);
   return hipGetLastError();
 }
 

@@ -253,10 +253,10 @@ hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, const void *qt, co
   const int nqb = (S + BM - 1) / BM;
   dim3 grid(nqb * BH);
   if (d == 128)
-    k_attn_fwd_mfma<128><<<grid, kThreads, 0, st>>>(S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+    lh::launch(k_attn_fwd_mfma<128>, grid, kThreads, 0, st, S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
                                                     (const uint16_t *)vt, ot, lse);
   else
-    k_attn_fwd_mfma<64><<<grid, kThreads, 0, st>>>(S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
+    lh::launch(k_attn_fwd_mfma<64>, grid, kThreads, 0, st, S, Sq, BH, (const uint16_t *)qt, (const uint16_t *)kt,
                                                    (const uint16_t *)vt, ot, lse);
   return hipGetLastError();
 }

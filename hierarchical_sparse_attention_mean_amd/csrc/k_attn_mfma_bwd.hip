@@ -488,11 +488,11 @@ hipError_t launch_attn_bwd_mfma(int d, int BH, int S, int Sv, const void *qt, co
   const uint16_t *g = (const uint16_t *)dotb;
   dim3 gq(((S + kDqBM - 1) / kDqBM) * BH), gk(((S + kKvBK - 1) / kKvBK) * BH);
   if (part == 0) {   // dQ~
-    if (d == 128) k_attn_bwd_dq<128><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dqt);
-    else k_attn_bwd_dq<64><<<gq, kDqThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dqt);
+    if (d == 128) lh::launch(k_attn_bwd_dq<128>, gq, kDqThreads, 0, st, S, Sv, BH, q, k, v, g, rows, dqt);
+    else lh::launch(k_attn_bwd_dq<64>, gq, kDqThreads, 0, st, S, Sv, BH, q, k, v, g, rows, dqt);
   } else {           // dK~, dV~
-    if (d == 128) k_attn_bwd_dkdv<128><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);
-    else k_attn_bwd_dkdv<64><<<gk, kKvThreads, 0, st>>>(S, Sv, BH, q, k, v, g, rows, dkt, dvt);
+    if (d == 128) lh::launch(k_attn_bwd_dkdv<128>, gk, kKvThreads, 0, st, S, Sv, BH, q, k, v, g, rows, dkt, dvt);
+    else lh::launch(k_attn_bwd_dkdv<64>, gk, kKvThreads, 0, st, S, Sv, BH, q, k, v, g, rows, dkt, dvt);
   }
   return hipGetLastError();
 }

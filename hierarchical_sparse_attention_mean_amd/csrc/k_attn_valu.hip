@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void k_attn_dkv_valu(int S, int Sq, const T *_
 hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st) {
   dim3 grid((S + BM - 1) / BM, BH);
-#define LH_FWD(T, D) k_attn_fwd_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, ot, lse)
+#define LH_FWD(T, D) lh::launch(k_attn_fwd_valu<T, D>, grid, 256, 0, st, S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, ot, lse)
   if (io == LH_BF16) {
     if (d == 128) LH_FWD(uint16_t, 128);
     else LH_FWD(uint16_t, 64);
@@ -247,10 +247,10 @@ hipError_t launch_attn_bwd_valu(int io, int d, int BH, int S, int Sq, const void
 #define LH_BWD(T, D)                                                                                            \
   do {                                                                                                          \
     if (part == 0)                                                                                              \
-      k_attn_dq_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,     \
+      lh::launch(k_attn_dq_valu<T, D>, grid, 256, 0, st, S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,     \
                                                  delta, dqt);                                                   \
     else                                                                                                        \
-      k_attn_dkv_valu<T, D><<<grid, 256, 0, st>>>(S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,    \
+      lh::launch(k_attn_dkv_valu<T, D>, grid, 256, 0, st, S, Sq, (const T *)qt, (const T *)kt, (const T *)vt, lse, dot,    \
                                                   delta, dkt, dvt);                                             \
   } while (0)
   if (io == LH_BF16) {

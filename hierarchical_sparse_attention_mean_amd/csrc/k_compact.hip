@@ -196,9 +196,9 @@ hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, c
   char *wsb = reinterpret_cast<char *>(ws);
   int *tc = reinterpret_cast<int *>(wsb + w.tilecount);
   dim3 grid(s.ntile, s.BH);
-  k_compact_count<<<grid, kThreads, 0, st>>>(s, flags, tc);
+  lh::launch(k_compact_count, grid, kThreads, 0, st, s, flags, tc);
 #define LH_GATHER(T, D)                                                                                         \
-  k_compact_gather<T, D><<<grid, kThreads, 0, st>>>(s, (const T *)q, (const T *)k, (const T *)v, wsb, w, flags, \
+  lh::launch(k_compact_gather<T, D>, grid, kThreads, 0, st, s, (const T *)q, (const T *)k, (const T *)v, wsb, w, flags, \
                                                     tc, slot, coords, (T *)qt, (T *)kt, (T *)vt)
   if (s.io == LH_BF16) {
     if (s.d == 128) LH_GATHER(uint16_t, 128);

@@ -420,11 +420,11 @@ int gemm_blocks(const GemmArgs &g, int io) {
 template <bool AKM, bool BKM>
 void launch_kinds(const GemmArgs &g, int io, int out_dtype, const dim3 &grid, hipStream_t st) {
   if (io == LH_BF16) {
-    if (out_dtype == LH_BF16) k_gemm_mfma<AKM, BKM, LH_BF16><<<grid, kGThreads, 0, st>>>(g);
-    else k_gemm_mfma<AKM, BKM, LH_F32><<<grid, kGThreads, 0, st>>>(g);
+    if (out_dtype == LH_BF16) lh::launch(k_gemm_mfma<AKM, BKM, LH_BF16>, grid, kGThreads, 0, st, g);
+    else lh::launch(k_gemm_mfma<AKM, BKM, LH_F32>, grid, kGThreads, 0, st, g);
   } else {
-    if (out_dtype == LH_BF16) k_gemm_f32<AKM, BKM, LH_BF16><<<grid, 256, 0, st>>>(g);
-    else k_gemm_f32<AKM, BKM, LH_F32><<<grid, 256, 0, st>>>(g);
+    if (out_dtype == LH_BF16) lh::launch(k_gemm_f32<AKM, BKM, LH_BF16>, grid, 256, 0, st, g);
+    else lh::launch(k_gemm_f32<AKM, BKM, LH_F32>, grid, 256, 0, st, g);
   }
 }
 
@@ -443,7 +443,7 @@ hipError_t launch_gemm(const GemmArgs &g, bool akm, bool bkm, int io, int out_dt
 
 hipError_t launch_split_reduce(const float *part, int nparts, int M, int N, const MatView &out, hipStream_t st) {
   const long long n4 = (long long)M * N / 4;
-  k_split_reduce<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(part, nparts, M, N, out);
+  lh::launch(k_split_reduce, (unsigned)((n4 + 255) / 256), 256, 0, st, part, nparts, M, N, out);
   return hipGetLastError();
 }
 

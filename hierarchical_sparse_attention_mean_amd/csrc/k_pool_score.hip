@@ -248,13 +248,13 @@ static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *
                           const FwdWs &w, float *scores, hipStream_t st) {
   const T *qq = (const T *)q, *kk = (const T *)k, *vv = (const T *)v;
   if (s.L <= 2)
-    k_pool_score<T, D, 2><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 2>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else if (s.L == 3)
-    k_pool_score<T, D, 3><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 3>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else if (s.L == 4)
-    k_pool_score<T, D, 4><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 4>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else
-    k_pool_score<T, D, kMaxL><<<grid, 256, 0, st>>>(s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, kMaxL>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
 }
 
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,

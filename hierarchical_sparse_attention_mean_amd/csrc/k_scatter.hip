@@ -672,8 +672,8 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
     dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);
 #define LH_SC(D, LM)                                                                                 \
   do {                                                                                               \
-    k_scatter_hi<D, LM><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);                             \
-    k_scatter_lo<D, LM><<<glo, 256, 0, st>>>(s, slot, coords, ot, o, o_dtype);                      \
+    lh::launch(k_scatter_hi<D, LM>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                             \
+    lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);                      \
   } while (0)
     if (s.d == 128) {
       if (s.L <= 3) LH_SC(128, 3);
@@ -689,8 +689,8 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
 #undef LH_SC
   } else {
     dim3 grid((unsigned)((s.N + 1 + per - 1) / per), s.BH);       // u = 0 .. N
-    if (s.d == 128) k_scatter<128><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);
-    else k_scatter<64><<<grid, 256, 0, st>>>(s, slot, ot, o, o_dtype);
+    if (s.d == 128) lh::launch(k_scatter<128>, grid, 256, 0, st, s, slot, ot, o, o_dtype);
+    else lh::launch(k_scatter<64>, grid, 256, 0, st, s, slot, ot, o, o_dtype);
   }
   return hipGetLastError();
 }
@@ -713,7 +713,7 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
       const int nwg = (int)((s.N + 1 + span - 1) / span);
       dim3 grid((unsigned)(nwg + 1), s.BH);
 #define LH_SW(D, B, G, LG) \
-  k_scatter_bwd_walk<D, B, G, LG><<<grid, 256, 0, st>>>(s, nwg, dout, dout_dtype, slot, ot, dot32, dotb, delta, lse, rows)
+  lh::launch(k_scatter_bwd_walk<D, B, G, LG>, grid, 256, 0, st, s, nwg, dout, dout_dtype, slot, ot, dot32, dotb, delta, lse, rows)
 #define LH_SWG(D, B)                          \
   do {                                        \
     if (s.p == 4) {                           \
@@ -741,7 +741,7 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
   // bf16 mode also writes the zero padding rows / columns up to Sv (a multiple of 64)
   const int spb = 256 / (s.d / 8);
   dim3 grid((unsigned)(((s.io == LH_BF16 ? s.Sv : s.S) + spb - 1) / spb), s.BH);
-#define LH_SB(D, B) k_scatter_bwd<D, B><<<grid, 256, 0, st>>>(s, dout, dout_dtype, coords, ot, dot32, dotb, delta, lse, rows)
+#define LH_SB(D, B) lh::launch(k_scatter_bwd<D, B>, grid, 256, 0, st, s, dout, dout_dtype, coords, ot, dot32, dotb, delta, lse, rows)
   if (s.d == 128) {
     if (bf) LH_SB(128, true);
     else LH_SB(128, false);
@@ -758,7 +758,7 @@ hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, co
   const int per = 256 / (s.d / 8);
   if (s.p >= 4 && (s.p & (s.p - 1)) == 0) {
     dim3 grid((unsigned)(((s.N + 3) / 4 + per - 1) / per), s.BH, 3);
-#define LH_PB(D, LM) k_pool_bwd_g4<D, LM><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype)
+#define LH_PB(D, LM) lh::launch(k_pool_bwd_g4<D, LM>, grid, 256, 0, st, s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype)
     if (s.d == 128) {
       if (s.L <= 3) LH_PB(128, 3);
       else if (s.L == 4) LH_PB(128, 4);
@@ -774,8 +774,8 @@ hipError_t launch_pool_bwd(const Shape &s, const int *slot, const float *dqt, co
   } else {
     const long long n = (long long)s.N * (s.d / 8);
     dim3 grid((unsigned)((n + 255) / 256), s.BH);
-    if (s.d == 128) k_pool_bwd<128><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);
-    else k_pool_bwd<64><<<grid, 256, 0, st>>>(s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);
+    if (s.d == 128) lh::launch(k_pool_bwd<128>, grid, 256, 0, st, s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);
+    else lh::launch(k_pool_bwd<64>, grid, 256, 0, st, s, slot, dqt, dkt, dvt, dq, dk, dv, grad_dtype);
   }
   return hipGetLastError();
 }

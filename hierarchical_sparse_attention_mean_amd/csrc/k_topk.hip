@@ -411,9 +411,9 @@ hipError_t launch_topk(const Shape &s, void *ws, const FwdWs &w, const float *sc
                        hipStream_t st) {
   char *wsb = reinterpret_cast<char *>(ws);
   const bool partial = s.Bsel > 0 && s.Bsel < s.E;
-  if (partial) k_topk_hist<<<dim3(topk_blocks(s.E, kHistBlocks), s.BH), kTopkThreads, 0, st>>>(s, wsb, w, scores);
-  k_topk_filter<<<dim3(topk_blocks(s.P, kFilterBlocks), s.BH), kTopkThreads, 0, st>>>(s, wsb, w, scores, flags);
-  if (partial) k_topk_refine<<<dim3(kRefineBlocks, s.BH), kRefineThreads, 0, st>>>(s, wsb, w, flags);
+  if (partial) lh::launch(k_topk_hist, dim3(topk_blocks(s.E, kHistBlocks), s.BH), kTopkThreads, 0, st, s, wsb, w, scores);
+  lh::launch(k_topk_filter, dim3(topk_blocks(s.P, kFilterBlocks), s.BH), kTopkThreads, 0, st, s, wsb, w, scores, flags);
+  if (partial) lh::launch(k_topk_refine, dim3(kRefineBlocks, s.BH), kRefineThreads, 0, st, s, wsb, w, flags);
   return hipGetLastError();
 }
 

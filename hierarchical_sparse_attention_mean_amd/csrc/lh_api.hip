@@ -15,6 +15,8 @@
 #include "lh_internal.h"
 
 namespace lh {
+thread_local LaunchTiming *t_launch_timing = nullptr;
+
 hipError_t launch_attn_fwd_valu(int io, int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
                                 float *ot, float *lse, hipStream_t st);
 hipError_t launch_attn_fwd_mfma(int d, int BH, int S, int Sq, const void *qt, const void *kt, const void *vt,
@@ -49,46 +51,45 @@ void timing_clear() {
   t_spans.clear();
 }
 
-// Brackets the launches of one stage with events on the stage's stream while
-// timing is on; does nothing otherwise, or for a negative stage (a call that
-// creates nothing).  An event that cannot be created or recorded drops that
-// span from the timing (the launches are unaffected).  The events only time:
-// they are created without the system-scope fence (cache writeback and
-// invalidation) that a default event performs when recorded, which would
-// otherwise stall the next stage's first launch by microseconds.
-hipError_t timing_event(hipEvent_t *e) { return hipEventCreateWithFlags(e, hipEventDisableSystemFence); }
-
+// Times the launches of one stage while timing is on; does nothing otherwise,
+// or for a negative stage (a call that creates nothing).  The launches inside
+// the span carry its events (lh::launch): the start event on the first kernel,
+// the stop event on every kernel, the last one's standing.  A span with no
+// launch, or whose events cannot be created, is dropped from the timing (the
+// launches are unaffected).
 class Span {
  public:
-  Span(int stage, hipStream_t s) : stage_(stage), s_(s) {
+  Span(int stage, hipStream_t s) : stage_(stage) {
+    (void)s;
     if (!t_timing || stage < 0) return;
-    if (timing_event(&start_) != hipSuccess) start_ = nullptr;
-    else if (hipEventRecord(start_, s_) != hipSuccess) {
-      (void)hipEventDestroy(start_);
-      start_ = nullptr;
+    if (hipEventCreate(&lt_.start) != hipSuccess) return;
+    if (hipEventCreate(&lt_.stop) != hipSuccess) {
+      (void)hipEventDestroy(lt_.start);
+      return;
     }
+    lt_.started = false;
+    prev_ = lh::t_launch_timing;
+    lh::t_launch_timing = &lt_;
+    open_ = true;
   }
   ~Span() {
-    if (!start_) return;
-    hipEvent_t stop;
-    if (timing_event(&stop) != hipSuccess) {
-      (void)hipEventDestroy(start_);
-      return;
+    if (!open_) return;
+    lh::t_launch_timing = prev_;
+    if (lt_.started) {
+      t_spans.push_back({stage_, lt_.start, lt_.stop});
+    } else {
+      (void)hipEventDestroy(lt_.start);
+      (void)hipEventDestroy(lt_.stop);
     }
-    if (hipEventRecord(stop, s_) != hipSuccess) {
-      (void)hipEventDestroy(start_);
-      (void)hipEventDestroy(stop);
-      return;
-    }
-    t_spans.push_back({stage_, start_, stop});
   }
   Span(const Span &) = delete;
   Span &operator=(const Span &) = delete;
 
  private:
   int stage_;
-  hipStream_t s_;
-  hipEvent_t start_ = nullptr;
+  bool open_ = false;
+  lh::LaunchTiming lt_{};
+  lh::LaunchTiming *prev_ = nullptr;
 };
 
 lh_status fail(lh_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -4,6 +4,7 @@
 // length (Sec. 3.5, Eq. 8).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -146,6 +147,30 @@ __device__ __forceinline__ unsigned long long make_key(float qk, float kq, int f
   const float r = fmaxf(qk, kq);
   const unsigned int g = (qk >= kq) ? (unsigned int)f : (unsigned int)(P + f);
   return ((unsigned long long)__float_as_uint(r) << 32) | (unsigned long long)(0xFFFFFFFFu - g);
+}
+
+// ---- kernel launches ----
+// Stage timing of the calling host thread: while a timed stage is open (see
+// lh_timing_begin), every launch carries the stage's stop event and the first
+// one also its start event, recorded by the kernel dispatches themselves
+// (hipExtLaunchKernel), so timing adds no packets between the kernels.
+struct LaunchTiming {
+  hipEvent_t start, stop;
+  bool started;   // a launch has carried the start event
+};
+extern thread_local LaunchTiming *t_launch_timing;   // null unless a timed stage is open
+
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arguments");
+  LaunchTiming *lt = t_launch_timing;
+  if (!lt) {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, static_cast<KArgs>(args)...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, lt->started ? nullptr : lt->start, lt->stop, 0,
+                        static_cast<KArgs>(args)...);
+  lt->started = true;
 }
 
 // ---- launchers (each enqueues on `st`, returns hipGetLastError()) ----
