@@ -19,7 +19,9 @@ Prints one JSON line (rank 0).  Besides the contract fields it carries:
   cpu_baseline  the fp64 oracle on one head of the same workload (fwd + bwd),
                 on this host's cores, scaled to the layer's tokens/s
   extra         per-stage times (with algorithmic bytes and achieved GB/s for the
-                memory-bound stages), forward-only time, the dense causal
+                memory-bound stages), forward-only time, the attention backward's
+                algorithmic rate (its 5 products over the dQ and dK/dV kernels'
+                time, which execute 7), the dense causal
                 attention kernels at S = N (one forward and one backward; skipped
                 with --no-dense), and (with --layer) the
                 projection-inclusive layer (X -> W_Q, W_K, W_V -> Lighthouse ->
@@ -414,8 +416,13 @@ def main() -> int:
     traffic = counter_traffic(dom, args.config)
     log(f"[bench] dominant kernel {dom}: {dom_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s")
 
+    # the backward's algorithmic products (5: S, dP, P^T dO, dS^T Q, dS K) over the time of both kernels that
+    # run them (7 executed: the dQ kernel recomputes S and dP so that no kernel needs floating-point atomics)
+    bwd_ms = stage_ms["attn_bwd_dq"]["ms_per_step"] + stage_ms["attn_bwd_dkdv"]["ms_per_step"]
+    bwd_alg = attention_flops(S, d, BH, 5) / (bwd_ms * 1e-3) / 1e12
     extra = {"ms_forward": ms_fwd, "ms_backward": ms - ms_fwd, "stages": stage_ms,
-             "tokens_per_s_forward": B * N / (ms_fwd * 1e-3)}
+             "tokens_per_s_forward": B * N / (ms_fwd * 1e-3),
+             "attn_bwd_algorithmic_tflops": bwd_alg, "attn_bwd_algorithmic_frac": bwd_alg / PEAK_BF16_TFLOPS}
     stream = torch.cuda.current_stream()
     if not args.no_dense:
         # the same attention kernels on the full sequence (S = N): dense causal attention forward and backward
