@@ -13,9 +13,9 @@
 // i = floor((t+1) / p^l) - 1, so each output element pulls its <= L
 // contributions and owns its accumulator.
 //
-// When p is a power of two >= 4 the scatter runs in two passes (coarser levels
-// for every position, then the few positions with a selected level-0 entry);
-// see k_scatter_hi / k_scatter_lo.
+// When p is a power of two the scatter runs in two passes (coarser levels for
+// every position, then the few positions with a selected level-0 entry); see
+// k_scatter_hi / k_scatter_lo.
 //
 // Adjoints (Sec. 3.2: gradients flow through scatter, attention, gather and
 // pool; the selection is frozen):
@@ -117,15 +117,15 @@ __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict_
 
 constexpr int kScatterGroups = 2;   // groups of 4 positions per thread in k_scatter_hi
 
-// p a power of two, p >= 4 (so every p^l with l >= 1 is a multiple of 4), in
-// two passes.
+// p a power of two, in two passes.
 //   k_scatter_hi   one thread per (NG groups of 4 positions, 8-element chunk):
 //                  the positions u = u0 .. u0 + 3 (u = t + 1, u0 a multiple of
-//                  4) share their entry of every level l >= 1 (i = (u0 >> l
-//                  log2 p) - 1), so a group needs one slot lookup and one row
-//                  per coarser level.  All lookups of the thread's groups are
-//                  issued first, then all rows.  Writes every position's sum
-//                  over its coarser levels.
+//                  4) share their entry of every level l with p^l >= 4
+//                  (i = (u0 >> l log2 p) - 1), so a group needs one slot lookup
+//                  and one row per such level; at p = 2 (P2) level 1 has one
+//                  entry per pair of the group's positions, two rows.  All
+//                  lookups of the thread's groups are issued first, then all
+//                  rows.  Writes every position's sum over its coarser levels.
 //   k_scatter_lo   one thread per (gathered row, 8-element chunk); rows of
 //                  level 0 (a few percent of them) rewrite their position's
 //                  output with the full sum, their own row included.
@@ -169,7 +169,7 @@ __device__ __forceinline__ void fixed_out(const float (&xs)[LM][8], const bool (
   }
 }
 
-template <int D, int LM>
+template <int D, int LM, bool P2>
 __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restrict__ slot,
                                                     const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
   constexpr int C8 = D / 8;
@@ -180,7 +180,9 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
   const int lg = __builtin_ctz(s.p);
   const int *sl = slot + (long long)h * s.P;
   const float *ob = ot + (long long)h * s.S * D + c * 8;
-  int u0[NG], mh[NG][LM];
+  // mh[g][l]: the group's entry of level l (at P2, level 1: its first pair's);
+  // m1[g]: at P2, the level-1 entry of its second pair (u0 + 2, u0 + 3)
+  int u0[NG], mh[NG][LM], m1[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     u0[g] = 4 * (blockIdx.x * (GPP * NG) + g * GPP + threadIdx.x / C8);
@@ -192,13 +194,18 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
         if (i >= 0) mh[g][l] = sl[s.off[l] + i];
       }
     }
+    m1[g] = -1;
+    if (P2 && s.L > 1 && u0[g] + 2 <= s.N) m1[g] = sl[s.off[1] + (u0[g] >> 1)];   // i = (u0 + 2) / 2 - 1
   }
-  float xs[NG][LM][8];
+  float xs[NG][LM][8], x1[P2 ? NG : 1][8];
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+  for (int g = 0; g < NG; ++g) {
 #pragma unroll
     for (int l = 1; l < LM; ++l)
       if (mh[g][l] >= 0) load_row8(ob + (long long)mh[g][l] * D, xs[g][l]);
+    if constexpr (P2)
+      if (m1[g] >= 0) load_row8(ob + (long long)m1[g] * D, x1[g]);
+  }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     bool has[LM];
@@ -207,9 +214,20 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
     float q[8];
     fixed_out<LM>(xs[g], has, q);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < (P2 ? 2 : 4); ++r) {
       const int t = u0[g] + r - 1;
       if (t >= 0 && t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
+    }
+    if constexpr (P2) {   // the second pair: its own level-1 row
+      has[1] = m1[g] >= 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[g][1][e] = x1[g][e];
+      fixed_out<LM>(xs[g], has, q);
+#pragma unroll
+      for (int r = 2; r < 4; ++r) {
+        const int t = u0[g] + r - 1;
+        if (t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
+      }
     }
   }
 }
@@ -666,26 +684,30 @@ __global__ __launch_bounds__(256) void k_pool_bwd_g4(Shape s, const int *__restr
 hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, const float *ot, void *o,
                           int o_dtype, hipStream_t st) {
   const int per = 256 / (s.d / 8);   // positions (or groups of 4 positions) per pass of a work-group
-  if (s.p >= 4 && (s.p & (s.p - 1)) == 0) {
+  if (s.p >= 2 && (s.p & (s.p - 1)) == 0 && (s.p >= 4 || (s.N & 1) == 0)) {
     const int gpb = per * kScatterGroups;
     dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // groups u0 = 0, 4, ..., <= N
     dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);
-#define LH_SC(D, LM)                                                                                 \
+#define LH_SC(D, LM, P2)                                                                             \
   do {                                                                                               \
-    lh::launch(k_scatter_hi<D, LM>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                             \
-    lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);                      \
+    lh::launch(k_scatter_hi<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                  \
+    lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);               \
+  } while (0)
+#define LH_SCL(D, P2)                   \
+  do {                                  \
+    if (s.L <= 3) LH_SC(D, 3, P2);      \
+    else if (s.L == 4) LH_SC(D, 4, P2); \
+    else if (s.L == 5) LH_SC(D, 5, P2); \
+    else LH_SC(D, kMaxL, P2);           \
   } while (0)
     if (s.d == 128) {
-      if (s.L <= 3) LH_SC(128, 3);
-      else if (s.L == 4) LH_SC(128, 4);
-      else if (s.L == 5) LH_SC(128, 5);
-      else LH_SC(128, kMaxL);
+      if (s.p == 2) LH_SCL(128, true);
+      else LH_SCL(128, false);
     } else {
-      if (s.L <= 3) LH_SC(64, 3);
-      else if (s.L == 4) LH_SC(64, 4);
-      else if (s.L == 5) LH_SC(64, 5);
-      else LH_SC(64, kMaxL);
+      if (s.p == 2) LH_SCL(64, true);
+      else LH_SCL(64, false);
     }
+#undef LH_SCL
 #undef LH_SC
   } else {
     dim3 grid((unsigned)((s.N + 1 + per - 1) / per), s.BH);       // u = 0 .. N
