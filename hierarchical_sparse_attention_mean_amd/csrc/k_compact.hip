@@ -10,12 +10,17 @@
 // base positions of "selected entries ending here".
 //
 //   k_compact_count   per tile of base positions: number of selected entries
-//                     ending in the tile.
-//   k_compact_gather  tile offset = sum of the earlier tiles' counts; block scan
+//                     ending in the tile (one wavefront per tile).
+//   k_compact_slots   tile offset = sum of the earlier tiles' counts; block scan
 //                     inside the tile; writes the slot map (-1 for unselected
-//                     entries), the sorted flat coordinates, and copies the rows
-//                     of Q~, K~, V~ into place (head stride Sv = S rounded up to
-//                     a multiple of 64, rows S..Sv-1 zero).
+//                     entries) and the sorted flat coordinates.
+//   k_gather_rows     one thread per 8-element piece of a gathered row: copies
+//                     the rows of Q~, K~, V~ named by the coordinates into place
+//                     (head stride Sv = S rounded up to a multiple of 64, rows
+//                     S..Sv-1 zero).  A flat grid over the rows, so the copy
+//                     keeps every compute unit busy at any tile count.
+#include <type_traits>
+
 #include "lh_internal.h"
 
 namespace lh {
@@ -23,16 +28,50 @@ namespace lh {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPer = kCompactTile / kThreads;   // positions per thread
+constexpr int kRowsPerThread = 1;   // gathered rows copied per thread
 
-__device__ __forceinline__ int count_at(const Shape &s, const uint8_t *fl, int t) {
-  int c = fl[t];
-  for (int l = 1; l < s.L; ++l) {
-    if ((t + 1) % s.pw[l] != 0) break;
-    c += fl[s.off[l] + (t + 1) / s.pw[l] - 1];
+// One wavefront per tile [T0, T1) of base positions.  The entries of level l
+// ending in the tile are the contiguous run i in [T0 / p^l, T1 / p^l) (integer
+// division), so the count is a sum of flag bytes over one run per level; the
+// level-0 run of a whole, 16-byte aligned tile is read 16 flags per lane
+// (flags are 0 or 1, so a popcount of the 16 bytes counts them).
+constexpr int kCountWaves = kThreads / 64;   // tiles per work-group
+
+__global__ __launch_bounds__(kThreads) void k_compact_count(Shape s, const uint8_t *__restrict__ flags,
+                                                            int *__restrict__ tilecount) {
+  static_assert(kCompactTile == 64 * 16, "16 level-0 flags per lane");
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * kCountWaves + (threadIdx.x >> 6);
+  if (tile >= s.ntile) return;
+  const uint8_t *fl = flags + (long long)h * s.P;
+  const int T0 = tile * kCompactTile, T1 = min(s.N, T0 + kCompactTile);
+  int c = 0;
+  if (T1 - T0 == kCompactTile && (reinterpret_cast<uintptr_t>(fl + T0) & 15) == 0) {
+    const uint4 f4 = *reinterpret_cast<const uint4 *>(fl + T0 + 16 * lane);
+    c = __popc(f4.x) + __popc(f4.y) + __popc(f4.z) + __popc(f4.w);
+  } else {
+    for (int t = T0 + lane; t < T1; t += 64) c += fl[t];
   }
-  return c;
+  for (int l = 1; l < s.L; ++l) {
+    const int a = T0 / s.pw[l], b = T1 / s.pw[l];
+    for (int i = a + lane; i < b; i += 64) c += fl[s.off[l] + i];
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) c += __shfl_xor(c, m);
+  if (lane == 0) tilecount[(long long)h * s.ntile + tile] = c;
 }
+
+// One work-group per tile, kPer = 4 base positions per thread.  The entries of
+// level l >= 1 ending at the thread's positions [t0, t1) are the run
+// i in [t0 / p^l, t1 / p^l), at most two entries (p >= 2); the thread loads its
+// level-0 flags and each level's run once, as bits, together with its share of
+// the earlier tiles' counts (the tile's offset).  One block sum and one block
+// scan then give each thread its first slot, and the thread walks its
+// positions in order (finer level first at each) writing the slot map and the
+// coordinates from those bits.
+constexpr int kPer = kCompactTile / kThreads;   // positions per thread
+static_assert(kPer == 4, "four level-0 flags per thread, at most two entries of a coarser level");
 
 __device__ __forceinline__ int block_sum(int v, int *red) {
   const int t = threadIdx.x;
@@ -45,45 +84,37 @@ __device__ __forceinline__ int block_sum(int v, int *red) {
   return tot;
 }
 
-__global__ __launch_bounds__(kThreads) void k_compact_count(Shape s, const uint8_t *__restrict__ flags,
-                                                            int *__restrict__ tilecount) {
-  __shared__ int red[kThreads / 64];
-  const int h = blockIdx.y;
-  const uint8_t *fl = flags + (long long)h * s.P;
-  const int t0 = blockIdx.x * kCompactTile + threadIdx.x * kPer;
-  int c = 0;
-  for (int e = 0; e < kPer; ++e)
-    if (t0 + e < s.N) c += count_at(s, fl, t0 + e);
-  const int tot = block_sum(c, red);
-  if (threadIdx.x == 0) tilecount[(long long)h * s.ntile + blockIdx.x] = tot;
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *__restrict__ q, const T *__restrict__ k,
-                                                            const T *__restrict__ v, const char *__restrict__ ws,
-                                                            FwdWs w, const uint8_t *__restrict__ flags,
+__global__ __launch_bounds__(kThreads) void k_compact_slots(Shape s, const uint8_t *__restrict__ flags,
                                                             const int *__restrict__ tilecount, int *__restrict__ slot,
-                                                            int *__restrict__ coords, T *__restrict__ qt,
-                                                            T *__restrict__ kt, T *__restrict__ vt) {
+                                                            int *__restrict__ coords) {
+  static_assert(2 * (LH_MAX_LEVELS - 1) <= 64, "two bits per coarser level");
   __shared__ int red[kThreads / 64];
   __shared__ int scan[kThreads / 64];   // wavefront totals
-  __shared__ int lflat[kCompactTile * 2];     // flat indices of this tile's slots (spills to global if more)
   const int h = blockIdx.y;
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
   const uint8_t *fl = flags + (long long)h * s.P;
-  // offset of this tile in the sub-sequence
+  const int t0 = tile * kCompactTile + tid * kPer;
+  const int t1 = min(s.N, t0 + kPer);   // the thread's positions [t0, t1), possibly empty
+  // level-0 flags: byte e of f0 is the flag of t0 + e
+  unsigned int f0 = 0;
+  if (t1 - t0 == kPer && (reinterpret_cast<uintptr_t>(fl + t0) & 3) == 0) {
+    f0 = *reinterpret_cast<const unsigned int *>(fl + t0);
+  } else {
+    for (int e = 0; e < t1 - t0; ++e) f0 |= (unsigned int)fl[t0 + e] << (8 * e);
+  }
+  // coarser levels: bits 2(l-1) and 2(l-1)+1 are the flags of the run's entries
+  unsigned long long cf = 0;
+  for (int l = 1; l < s.L; ++l) {
+    const int a = t0 / s.pw[l], b = t0 < t1 ? t1 / s.pw[l] : a;
+    const unsigned int x0 = a < b ? fl[s.off[l] + a] : 0u;
+    const unsigned int x1 = a + 1 < b ? fl[s.off[l] + a + 1] : 0u;
+    cf |= (unsigned long long)(x0 | (x1 << 1)) << (2 * (l - 1));
+  }
+  const int mine = __popc(f0) + __popcll(cf);
   int pre = 0;
   for (int i = tid; i < tile; i += kThreads) pre += tilecount[(long long)h * s.ntile + i];
   const int m0 = block_sum(pre, red);
-  // per-thread counts of its kPer positions, exclusive scan over the block
-  const int t0 = tile * kCompactTile + tid * kPer;
-  int cnt[kPer];
-  int mine = 0;
-  for (int e = 0; e < kPer; ++e) {
-    cnt[e] = (t0 + e < s.N) ? count_at(s, fl, t0 + e) : 0;
-    mine += cnt[e];
-  }
   // exclusive scan over the block: inclusive scan within each wavefront by
   // shuffles, then the wavefront totals (one barrier)
   const int lane = tid & 63, wv = tid >> 6;
@@ -95,95 +126,101 @@ __global__ __launch_bounds__(kThreads) void k_compact_gather(Shape s, const T *_
   }
   if (lane == 63) scan[wv] = incl;
   __syncthreads();
-  int wbase = 0, ntot = 0;
+  int wbase = 0;
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) {
-    wbase += i < wv ? scan[i] : 0;
-    ntot += scan[i];
-  }
+  for (int i = 0; i < kThreads / 64; ++i) wbase += i < wv ? scan[i] : 0;
   int m = m0 + wbase + incl - mine;
   int *sl = slot + (long long)h * s.P;
   int *co = coords + (long long)h * s.S;
+  int v0[kPer];   // level-0 slot-map entries of the thread's positions
+#pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int t = t0 + e;
-    if (t >= s.N) break;
+    v0[e] = -1;
+    if (t >= t1) continue;
     // entries ending at t, finer level first
-    {
-      const int f = t;
-      if (fl[f]) {
-        sl[f] = m;
-        co[m] = f;
-        if (m - m0 < kCompactTile * 2) lflat[m - m0] = f;
-        ++m;
-      } else {
-        sl[f] = -1;
-      }
+    if ((f0 >> (8 * e)) & 1u) {
+      v0[e] = m;
+      co[m++] = t;
     }
     for (int l = 1; l < s.L; ++l) {
       if ((t + 1) % s.pw[l] != 0) break;
-      const int f = s.off[l] + (t + 1) / s.pw[l] - 1;
-      if (fl[f]) {
+      const int i = (t + 1) / s.pw[l] - 1;
+      const int f = s.off[l] + i;
+      if ((cf >> (2 * (l - 1) + (i - t0 / s.pw[l]))) & 1ull) {
         sl[f] = m;
-        co[m] = f;
-        if (m - m0 < kCompactTile * 2) lflat[m - m0] = f;
-        ++m;
+        co[m++] = f;
       } else {
         sl[f] = -1;
       }
     }
   }
-  __syncthreads();
-  // row copies: CH threads per row, 8 elements each
-  constexpr int CH = D / 8;
-  constexpr int RPI = kThreads / CH;   // rows per iteration
-  const int j = tid % CH;
-  const int rr = tid / CH;
-  const long long hS = (long long)h * s.Sv;   // gathered rows: head stride Sv
-  for (int mm = rr; mm < ntot; mm += RPI) {
-    const int f = (mm < kCompactTile * 2) ? lflat[mm] : co[m0 + mm];
-    int l = 0;
-    while (l + 1 < s.L && f >= s.off[l + 1]) ++l;
-    const int i = f - s.off[l];
-    const T *sq, *sk, *sv;
-    if (l == 0) {
-      const long long base = ((long long)h * s.N + i) * D;
-      sq = q + base;
-      sk = k + base;
-      sv = v + base;
-    } else {
-      const long long base = ((long long)h * s.n[l] + i) * D;
-      sq = reinterpret_cast<const T *>(ws + w.lev[l][0]) + base;
-      sk = reinterpret_cast<const T *>(ws + w.lev[l][1]) + base;
-      sv = reinterpret_cast<const T *>(ws + w.lev[l][2]) + base;
-    }
-    const long long dst = (hS + m0 + mm) * D + j * 8;
-    if constexpr (sizeof(T) == 2) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(sq + j * 8);
-      const uint4 b = *reinterpret_cast<const uint4 *>(sk + j * 8);
-      const uint4 c = *reinterpret_cast<const uint4 *>(sv + j * 8);
-      *reinterpret_cast<uint4 *>(qt + dst) = a;
-      *reinterpret_cast<uint4 *>(kt + dst) = b;
-      *reinterpret_cast<uint4 *>(vt + dst) = c;
-    } else {
+  if (t1 - t0 == kPer && (reinterpret_cast<uintptr_t>(sl + t0) & 15) == 0) {
+    *reinterpret_cast<int4 *>(sl + t0) = make_int4(v0[0], v0[1], v0[2], v0[3]);
+  } else {
 #pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const float4 a = *reinterpret_cast<const float4 *>(sq + j * 8 + hlf * 4);
-        const float4 b = *reinterpret_cast<const float4 *>(sk + j * 8 + hlf * 4);
-        const float4 c = *reinterpret_cast<const float4 *>(sv + j * 8 + hlf * 4);
-        *reinterpret_cast<float4 *>(qt + dst + hlf * 4) = a;
-        *reinterpret_cast<float4 *>(kt + dst + hlf * 4) = b;
-        *reinterpret_cast<float4 *>(vt + dst + hlf * 4) = c;
+    for (int e = 0; e < kPer; ++e)
+      if (t0 + e < t1) sl[t0 + e] = v0[e];
+  }
+}
+
+// Row copies: gathered row m of head h is the pyramid entry coords[m] (rows
+// S..Sv-1 are written as zeros).  A thread copies one piece of 8 elements of
+// the row, the same piece of Q~, K~ and V~; CH = D / 8 threads per row.  The
+// level of an entry and the start of its level's rows are selected from the
+// shape by an unrolled scan over the levels (uniform in l, so the offsets stay
+// scalar).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_gather_rows(Shape s, const T *__restrict__ q, const T *__restrict__ k,
+                                                          const T *__restrict__ v, const char *__restrict__ ws,
+                                                          FwdWs w, const int *__restrict__ coords,
+                                                          T *__restrict__ qt, T *__restrict__ kt,
+                                                          T *__restrict__ vt) {
+  constexpr int CH = D / 8;
+  constexpr int RPB = kThreads / CH;   // rows per work-group and pass
+  using V8 = typename std::conditional<sizeof(T) == 2, uint4, float4>::type;
+  constexpr int NV = sizeof(T) == 2 ? 1 : 2;   // 16-byte vectors per piece
+  const int h = blockIdx.y;
+  const int j = threadIdx.x % CH;
+  V8 a[kRowsPerThread][NV], b[kRowsPerThread][NV], c[kRowsPerThread][NV];
+  // all rows' loads first, then all stores
+#pragma unroll
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int m = (blockIdx.x * kRowsPerThread + u) * RPB + threadIdx.x / CH;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) a[u][x] = b[u][x] = c[u][x] = V8{};
+    if (m >= s.S) continue;   // rows S..Sv-1: zeros
+    const int f = coords[(long long)h * s.S + m];
+    const T *bq = q, *bk = k, *bv = v;
+    long long r = (long long)h * s.N + f;
+#pragma unroll
+    for (int l = 1; l < LH_MAX_LEVELS; ++l) {
+      if (l >= s.L) break;
+      if (f >= s.off[l]) {
+        bq = reinterpret_cast<const T *>(ws + w.lev[l][0]);
+        bk = reinterpret_cast<const T *>(ws + w.lev[l][1]);
+        bv = reinterpret_cast<const T *>(ws + w.lev[l][2]);
+        r = (long long)h * s.n[l] + (f - s.off[l]);
       }
     }
+    const long long src = r * D + j * 8;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      a[u][x] = reinterpret_cast<const V8 *>(bq + src)[x];
+      b[u][x] = reinterpret_cast<const V8 *>(bk + src)[x];
+      c[u][x] = reinterpret_cast<const V8 *>(bv + src)[x];
+    }
   }
-  // zero the padding rows S..Sv-1 of the gathered rows
-  if (tile == s.ntile - 1) {
-    const int pad = s.Sv - s.S;
-    for (int idx = tid; idx < D * pad; idx += kThreads) {
-      const long long o = (hS + s.S) * D + idx;
-      qt[o] = T(0);
-      kt[o] = T(0);
-      vt[o] = T(0);
+#pragma unroll
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int m = (blockIdx.x * kRowsPerThread + u) * RPB + threadIdx.x / CH;
+    if (m >= s.Sv) continue;
+    const long long dst = ((long long)h * s.Sv + m) * D + j * 8;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      reinterpret_cast<V8 *>(qt + dst)[x] = a[u][x];
+      reinterpret_cast<V8 *>(kt + dst)[x] = b[u][x];
+      reinterpret_cast<V8 *>(vt + dst)[x] = c[u][x];
     }
   }
 }
@@ -195,11 +232,13 @@ hipError_t launch_compact_gather(const Shape &s, const void *q, const void *k, c
                                  void *kt, void *vt, hipStream_t st) {
   char *wsb = reinterpret_cast<char *>(ws);
   int *tc = reinterpret_cast<int *>(wsb + w.tilecount);
-  dim3 grid(s.ntile, s.BH);
-  lh::launch(k_compact_count, grid, kThreads, 0, st, s, flags, tc);
-#define LH_GATHER(T, D)                                                                                         \
-  lh::launch(k_compact_gather<T, D>, grid, kThreads, 0, st, s, (const T *)q, (const T *)k, (const T *)v, wsb, w, flags, \
-                                                    tc, slot, coords, (T *)qt, (T *)kt, (T *)vt)
+  lh::launch(k_compact_count, dim3((s.ntile + kCountWaves - 1) / kCountWaves, s.BH), kThreads, 0, st, s, flags, tc);
+  lh::launch(k_compact_slots, dim3(s.ntile, s.BH), kThreads, 0, st, s, flags, (const int *)tc, slot, coords);
+  const int rows = kRowsPerThread * kThreads / (s.d / 8);   // rows per row-copy work-group
+  const dim3 rgrid((s.Sv + rows - 1) / rows, s.BH);
+#define LH_GATHER(T, D)                                                                                          \
+  lh::launch(k_gather_rows<T, D>, rgrid, kThreads, 0, st, s, (const T *)q, (const T *)k, (const T *)v,          \
+             (const char *)wsb, w, (const int *)coords, (T *)qt, (T *)kt, (T *)vt)
   if (s.io == LH_BF16) {
     if (s.d == 128) LH_GATHER(uint16_t, 128);
     else LH_GATHER(uint16_t, 64);
