@@ -13,13 +13,18 @@
 //
 // Work mapping: grid plane z = 0, 1, 2 pools Q, K, V respectively; the Q and K
 // planes also compute the query and key scores.  A work-group of 256 threads
-// covers RG row-groups x CH column chunks of EL elements (EL = 8 up to four
+// covers RG row-groups x CH column chunks of EL elements (EL = 8 up to five
 // levels, 4 beyond, which halves the per-level accumulators so that more
 // wavefronts fit).  Row-group rg owns one coarsest window of G = p^(L-1)
 // consecutive rows and walks it top to bottom, reading its rows in batches
-// (2 rows up to three levels, 8 beyond) one batch ahead of their use, so
-// every pooled window and every max-pool lives in one thread's registers; only the norm of a row needs a reduction, across the CH lanes that
-// hold it (adjacent lanes of one wavefront, reduced with xor shuffles).
+// (2 rows up to three levels, 4 at five, 8 otherwise) one batch ahead of their
+// use, so every pooled window and every max-pool lives in one thread's
+// registers; only the norm of a row needs a reduction, across the CH lanes that
+// hold it (adjacent lanes of one wavefront, reduced with xor shuffles).  At
+// five levels (when p divides RG) the p sub-windows of a coarsest window are
+// walked by p row-groups of one work-group and the coarsest level is summed
+// from theirs through LDS, in sub-window order: a window of p^4 rows walked by
+// one row-group would leave too few threads for the memory system.
 #include "lh_internal.h"
 
 namespace lh {
@@ -104,16 +109,16 @@ template <int EL> struct Raw<float, EL> {
   }
 };
 
-template <typename T, int D, int ML>
+template <typename T, int D, int ML, bool SPLIT>
 __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict__ q, const T *__restrict__ k,
                                                     const T *__restrict__ v, char *__restrict__ ws, FwdWs w,
                                                     float *__restrict__ scores) {
-  constexpr int EL = ML <= 4 ? 8 : 4;   // elements per lane
+  constexpr int EL = ML <= 5 ? 8 : 4;   // elements per lane
   constexpr int CH = D / EL;            // threads per row
   constexpr int RG = 256 / CH;          // row-groups per work-group
   // rows of a window read per batch, two batches in flight (measured: short
   // windows favour occupancy, long ones more bytes in flight)
-  constexpr int NB = ML <= 3 ? 2 : 8;
+  constexpr int NB = ML <= 3 ? 2 : (ML == 5 ? 4 : 8);
   const int h = blockIdx.y;
   const int z = blockIdx.z;             // 0: Q and its scores, 1: K and its scores, 2: V
   const bool scored = z < 2;
@@ -121,7 +126,12 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   const int rg = threadIdx.x / CH;
   const int L = s.L;
   const int G = s.pw[L - 1];
-  const long long win = (long long)blockIdx.x * RG + rg;   // coarsest window index
+  // SPLIT: the p row-groups rg = p c .. p c + p - 1 of the work-group walk the
+  // p sub-windows of its coarsest window c, GW = G / p rows each
+  const int nsub = SPLIT ? s.p : 1;
+  const int sub = rg % nsub;
+  const int GW = G / nsub;
+  const long long win = (long long)blockIdx.x * (RG / nsub) + rg / nsub;   // coarsest window index
   const bool active = win < s.n[L - 1];
   const T *x = z == 0 ? q : (z == 1 ? k : v);
   const long long hoff = (long long)h * s.N * D;
@@ -143,10 +153,10 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
   }
   unsigned int umin = 0xFFFFFFFFu, umax = 0u;
 
-  const long long t0 = win * G;
-  // the rows of the window are read in batches of NB, one batch ahead of
+  const long long t0 = win * G + (long long)sub * GW;
+  // the rows of the (sub-)window are read in batches of NB, one batch ahead of
   // their use (rows past the window clamp to its last row, unused)
-  const long long last = active ? t0 + G - 1 : 0;
+  const long long last = active ? t0 + GW - 1 : 0;
   const T *xh = x + hoff + j * EL;
   Raw<T, EL> cur[NB], nxt[NB];
   auto load_batch = [&](Raw<T, EL>(&b)[NB], int r0) {
@@ -154,12 +164,12 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
     for (int u = 0; u < NB; ++u) b[u].load(xh + (active ? min(t0 + r0 + u, last) : 0) * D);
   };
   load_batch(cur, 0);
-  for (int r0 = 0; r0 < G; r0 += NB) {
-    if (r0 + NB < G) load_batch(nxt, r0 + NB);
+  for (int r0 = 0; r0 < GW; r0 += NB) {
+    if (r0 + NB < GW) load_batch(nxt, r0 + NB);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const int r = r0 + u;
-      if (r >= G) break;
+      const int r = r0 + u;   // GW is a multiple of p^l for every level l completed here
+      if (r >= GW) break;
       const long long t = t0 + r;
       float xr[EL];
       cur[u].unpack(xr);
@@ -218,6 +228,34 @@ __global__ __launch_bounds__(256) void k_pool_score(Shape s, const T *__restrict
 #pragma unroll
     for (int u = 0; u < NB; ++u) cur[u] = nxt[u];
   }
+  if constexpr (SPLIT) {
+    // acc[L-1], mx[L-1] hold this sub-window's level-(L-2) sum and max (L == ML); the
+    // first row-group of the window adds the p of them in sub-window order,
+    // as one walk over the whole window would
+    __shared__ float part[256][EL];
+    __shared__ float pmx[RG];
+    static_assert(!SPLIT || ML == 5, "split walks serve five levels (L == ML)");
+#pragma unroll
+    for (int e = 0; e < EL; ++e) part[threadIdx.x][e] = acc[ML - 1][e];
+    if (j == 0) pmx[rg] = mx[ML - 1];
+    __syncthreads();
+    if (sub == 0 && active) {
+      float tot[EL], m = 0.f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) tot[e] = 0.f;
+      for (int q = 0; q < nsub; ++q) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) tot[e] += part[threadIdx.x + q * CH][e];
+        m = fmaxf(m, pmx[rg + q]);
+      }
+      const float inv = 1.0f / (float)G;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) tot[e] *= inv;
+      VecN<T, EL>::store(reinterpret_cast<T *>(ws + w.lev[L - 1][z]) + ((long long)h * s.n[L - 1] + win) * D + j * EL,
+                         tot);
+      if (scored && j == 0) sc[s.off[L - 1] + (int)win] = m;
+    }
+  }
   if (L == 1 || !scored) return;
   // range of this work-group's candidate score bits (min > max if it has none);
   // the union over both streams' work-groups contains every key's upper half,
@@ -248,13 +286,17 @@ static void pool_score_ml(const Shape &s, dim3 grid, const void *q, const void *
                           const FwdWs &w, float *scores, hipStream_t st) {
   const T *qq = (const T *)q, *kk = (const T *)k, *vv = (const T *)v;
   if (s.L <= 2)
-    lh::launch(k_pool_score<T, D, 2>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 2, false>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else if (s.L == 3)
-    lh::launch(k_pool_score<T, D, 3>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 3, false>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else if (s.L == 4)
-    lh::launch(k_pool_score<T, D, 4>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, 4, false>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+  else if (s.L == 5 && pool_score_split(D, 5, s.p))
+    lh::launch(k_pool_score<T, D, 5, true>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+  else if (s.L == 5)
+    lh::launch(k_pool_score<T, D, 5, false>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
   else
-    lh::launch(k_pool_score<T, D, kMaxL>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
+    lh::launch(k_pool_score<T, D, kMaxL, false>, grid, 256, 0, st, s, qq, kk, vv, ws, w, scores);
 }
 
 hipError_t launch_pool_score(const Shape &s, const void *q, const void *k, const void *v, void *ws,

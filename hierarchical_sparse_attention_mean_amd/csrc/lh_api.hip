@@ -159,8 +159,8 @@ lh_status make_shape(int B, int H, int64_t N, int d, int L, int p, int64_t topk,
   s->Sv = (s->S + 63) & ~63;
   if ((int64_t)s->S * d >= ((int64_t)1 << 31)) return fail(LH_EUNSUPPORTED, "S*d must be < 2^31");
   s->ntile = (s->N + lh::kCompactTile - 1) / lh::kCompactTile;
-  const int rg = lh::pool_score_rowgroups(d, L);
-  s->npool = (s->n[L - 1] + rg - 1) / rg;
+  const int wpg = lh::pool_score_windows(d, L, p);
+  s->npool = (s->n[L - 1] + wpg - 1) / wpg;
   return LH_OK;
 }
 

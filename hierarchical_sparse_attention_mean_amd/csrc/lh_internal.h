@@ -31,12 +31,22 @@ struct Shape {
   int S;                     // gathered length per head
   int Sv;                    // row stride of the transposed copies: S rounded up to a multiple of 64
   int ntile;                 // compaction tiles per head
-  int npool;                 // pool+score work-groups per head and tensor (coarsest windows / row-groups)
+  int npool;                 // pool+score work-groups per head and tensor (coarsest windows / windows per work-group)
 };
 
-// Row-groups (coarsest windows) per pool+score work-group of 256 threads: a row
-// of d elements is spread over d / EL lanes, EL = 8 up to four levels, 4 beyond.
-__host__ __device__ inline int pool_score_rowgroups(int d, int L) { return 256 / (d / (L <= 4 ? 8 : 4)); }
+// Pool+score work-groups of 256 threads: a row of d elements is spread over
+// d / EL lanes (EL = 8 up to five levels, 4 beyond), so a work-group has
+// 256 / (d / EL) row-groups.  A row-group walks one coarsest window, or, at
+// five levels when p divides the row-group count, one of the p sub-windows of
+// a coarsest window (pool_score_split).
+__host__ __device__ inline int pool_score_rowgroups(int d, int L) { return 256 / (d / (L <= 5 ? 8 : 4)); }
+__host__ __device__ inline bool pool_score_split(int d, int L, int p) {
+  return L == 5 && pool_score_rowgroups(d, L) % p == 0;
+}
+// Coarsest windows per pool+score work-group.
+__host__ __device__ inline int pool_score_windows(int d, int L, int p) {
+  return pool_score_split(d, L, p) ? pool_score_rowgroups(d, L) / p : pool_score_rowgroups(d, L);
+}
 
 constexpr int kCompactTile = 1024;   // base positions per compaction work-group
 constexpr int kHistBins = 4096;      // first radix-select digit of the top-k

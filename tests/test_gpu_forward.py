@@ -146,6 +146,8 @@ def test_tiny_L1_dense(lh):
     (3072, 2, 4, 5, 1, 3),      # two levels
     (512, 3, 2, 0, 1, 1),       # k = 0: only the coarsest level
     (4096, 5, 2, 200, 1, 1),    # five levels
+    (3328, 5, 4, 16, 1, 2),     # five levels, p = 4: coarsest windows split over row-groups, ragged last work-group
+    (3240, 5, 3, 10, 1, 1),     # five levels, p = 3: coarsest windows walked whole
     (1944, 3, 3, 20, 1, 2),     # p = 3: a pooling factor that is not a power of two
 ])
 def test_shapes_fp32(lh, N, L, p, k, B, H):
