@@ -390,24 +390,23 @@ constexpr int kWalkCoarse = 2;   // most levels k_scatter_bwd_walk combines thro
 // entry (l, i) is the aligned block [(i+1) p^l, (i+2) p^l), so a walk over u
 // in aligned blocks meets every entry's range exactly once, like the pooling
 // walk of the forward: row group g of the work-group (C8 lanes, 8 columns
-// each) reads the dO rows of its GW = p^A consecutive positions once (in
-// batches of NB), sums the ranges of levels 0 .. A in registers (level l's sum
+// each) reads the dO rows of its GW = p^A consecutive positions once (all
+// loads issued together), sums the ranges of levels 0 .. A in registers (level l's sum
 // is the sum of its p children's, levels ascending), and on completing the
-// range of a selected entry writes its dO~ row and delta; the work-group then
-// forms the ranges of levels A+1 .. L-1 from its row groups' block sums through
-// LDS, in row-group order.  dO is read once (k_scatter_bwd reads a row once per
-// selected entry covering it, up to L times).  One extra work-group per head
-// writes the zero padding rows (bf16 mode).
+// range of a selected entry writes its dO~ row; the work-group then forms the
+// ranges of levels A+1 .. L-1 from its row groups' block sums through LDS, in
+// row-group order.  dO is read once (k_scatter_bwd reads a row once per
+// selected entry covering it, up to L times).  The walk reads no O~: delta and
+// the row pairs come from k_scatter_delta afterwards, so no step of the walk
+// waits on a load that depends on a slot.
 template <int D, bool BF16, int GW, int LG>
-__global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, int nwg, const void *__restrict__ dout,
-                                                          int dout_dtype, const int *__restrict__ slot,
-                                                          const float *__restrict__ ot, float *__restrict__ dot32,
-                                                          uint16_t *__restrict__ dotb, float *__restrict__ delta,
-                                                          const float *__restrict__ lse, float *__restrict__ rows) {
+__global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, const void *__restrict__ dout, int dout_dtype,
+                                                          const int *__restrict__ slot, float *__restrict__ dot32,
+                                                          uint16_t *__restrict__ dotb) {
   constexpr int C8 = D / 8;
   constexpr int RG = 256 / C8;
   constexpr int W = RG * GW;           // u positions per work-group
-  constexpr int NB = GW < 8 ? GW : 8;  // rows per batch
+  constexpr int NB = GW;               // rows per batch: all of the row group's rows in flight at once
   constexpr int A = __builtin_ctz(GW) / LG;   // levels 1 .. A summed in registers (p^A = GW)
   static_assert((1 << (A * LG)) == GW, "GW is a power of p");
   // slots of the block's entries of levels 1 .. A: level l has GW >> (l LG) of them, at sbase(l)
@@ -417,61 +416,27 @@ __global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, int nwg, cons
     return o;
   };
   constexpr int NSL = sbase(A + 1) > 0 ? sbase(A + 1) : 1;
-  __shared__ float part[RG][D + 4];
+  __shared__ __attribute__((aligned(16))) float part[RG][D + 4];   // rows of (D + 4) floats: 16-byte aligned
   const int h = blockIdx.y;
   const int c = threadIdx.x % C8, g = threadIdx.x / C8;
-  if (blockIdx.x == nwg) {   // bf16 mode: zero padding rows S .. Sv-1
-    if constexpr (BF16) {
-      for (int r = s.S + g; r < s.Sv; r += RG) {
-        *reinterpret_cast<uint4 *>(dotb + ((long long)h * s.Sv + r) * D + c * 8) = make_uint4(0u, 0u, 0u, 0u);
-        if (c == 0) *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + r)) = make_float2(0.f, 0.f);
-      }
-    }
-    return;
-  }
   const int *sl = slot + (long long)h * s.P;
   const int ub = blockIdx.x * W + g * GW;   // first u of this row group's block
   const long long dbase = ((long long)h * s.N) * D + c * 8;
 
-  // Output of entry slot m with range sum x (dO~ as the attention backward
-  // reads it, and delta = rowsum(dO~ o O~)); uniform over the row group.
-  auto emit_o = [&](int m, const float (&x)[8], const float (&o8)[8]) {
-    float y[8];
-    uint16_t hb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = x[e];
-      if constexpr (BF16) {
-        hb[e] = f32_to_bf16_rne(y[e]);
-        y[e] = bf16_to_f32(hb[e]);
-      }
-    }
-    float dl = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dl = fmaf(y[e], o8[e], dl);
-#pragma unroll
-    for (int xo = 1; xo < C8; xo <<= 1) dl += __shfl_xor(dl, xo);
+  // dO~ row of entry slot m with range sum x (rounded to bf16 in bf16 mode)
+  auto emit = [&](int m, const float (&x)[8]) {
     if constexpr (BF16) {
       uint4 w;
-      w.x = (unsigned)hb[0] | ((unsigned)hb[1] << 16);
-      w.y = (unsigned)hb[2] | ((unsigned)hb[3] << 16);
-      w.z = (unsigned)hb[4] | ((unsigned)hb[5] << 16);
-      w.w = (unsigned)hb[6] | ((unsigned)hb[7] << 16);
+      w.x = (unsigned)f32_to_bf16_rne(x[0]) | ((unsigned)f32_to_bf16_rne(x[1]) << 16);
+      w.y = (unsigned)f32_to_bf16_rne(x[2]) | ((unsigned)f32_to_bf16_rne(x[3]) << 16);
+      w.z = (unsigned)f32_to_bf16_rne(x[4]) | ((unsigned)f32_to_bf16_rne(x[5]) << 16);
+      w.w = (unsigned)f32_to_bf16_rne(x[6]) | ((unsigned)f32_to_bf16_rne(x[7]) << 16);
       *reinterpret_cast<uint4 *>(dotb + ((long long)h * s.Sv + m) * D + c * 8) = w;
-      if (c == 0)
-        *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + m)) =
-            make_float2(lse[(long long)h * s.S + m] * 1.4426950408889634f, dl);
     } else {
-      if (c == 0) delta[(long long)h * s.S + m] = dl;
       float *dst = dot32 + ((long long)h * s.S + m) * D + c * 8;
-      *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4 *>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4 *>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
     }
-  };
-  auto emit = [&](int m, const float (&x)[8]) {
-    float o8[8];
-    load_row8(ot + ((long long)h * s.S + m) * D + c * 8, o8);
-    emit_o(m, x, o8);
   };
   // slot of the entry of level l whose range ends at u, or -1
   auto slot_at = [&](int l, int u) {
@@ -485,18 +450,14 @@ __global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, int nwg, cons
 #pragma unroll
     for (int k = 0; k < (GW >> (l * LG)); ++k) msl[sbase(l) + k] = slot_at(l, ub + ((k + 1) << (l * LG)) - 1);
   // the entries of levels A+1 .. L-1 whose range this row group combines (see
-  // below) and their O~ rows, loaded ahead of the walk
+  // below), looked up ahead of the walk
   constexpr int NCO = kWalkCoarse;   // levels above A (the launcher dispatches L - 1 - A <= kWalkCoarse)
   int mco[NCO];
-  float oco[NCO][8];
 #pragma unroll
   for (int j = 0; j < NCO; ++j) {
     const int l = A + 1 + j;
     mco[j] = -1;
-    if (l < s.L && g < W / s.pw[l]) {
-      mco[j] = slot_at(l, blockIdx.x * W + (g + 1) * s.pw[l] - 1);
-      if (mco[j] >= 0) load_row8(ot + ((long long)h * s.S + mco[j]) * D + c * 8, oco[j]);
-    }
+    if (l < s.L && g < W / s.pw[l]) mco[j] = slot_at(l, blockIdx.x * W + (g + 1) * s.pw[l] - 1);
   }
   float acc[A + 1][8];   // acc[l]: running range sum of level l >= 1; acc[0]: the block sum
 #pragma unroll
@@ -571,14 +532,71 @@ __global__ __launch_bounds__(256) void k_scatter_bwd_walk(Shape s, int nwg, cons
   for (int j = 0; j < NCO; ++j) {
     if (mco[j] < 0) continue;   // no such level, range or selection
     const int per = s.pw[A + 1 + j] / GW;   // row groups per range of the level
+    // x = part[g per] + part[g per + 1] + ... element by element, in order;
+    // each partial row read as two 16-byte vectors, the loads independent
     float x[8];
+    auto get = [&](int r, float (&y)[8]) {
+      const float4 u = *reinterpret_cast<const float4 *>(&part[g * per + r][c * 8]);
+      const float4 v = *reinterpret_cast<const float4 *>(&part[g * per + r][c * 8 + 4]);
+      y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
+    };
+    get(0, x);
+#pragma unroll 4
+    for (int r = 1; r < per; ++r) {
+      float y[8];
+      get(r, y);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = part[g * per][c * 8 + e];
-      for (int r = 1; r < per; ++r) v += part[g * per + r][c * 8 + e];
-      x[e] = v;
+      for (int e = 0; e < 8; ++e) x[e] += y[e];
     }
-    emit_o(mco[j], x, oco[j]);
+    emit(mco[j], x);
+  }
+}
+
+// delta_m = rowsum(dO~_m o O~_m) with dO~ as the walk stored it (bf16 in bf16
+// mode), in the arithmetic k_scatter_bwd uses (an fma chain over a lane's 8
+// elements, then a xor-shuffle tree over the row's C8 lanes), so the two give
+// the same bits.  bf16 mode writes the row pair (LSE log2(e), delta) and zeros
+// on the padding rows S .. Sv-1 (dO~ and pair); fp32 mode writes delta.  One
+// thread per (row, 8 columns).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_scatter_delta(Shape s, const float *__restrict__ ot,
+                                                       const float *__restrict__ dot32, uint16_t *__restrict__ dotb,
+                                                       float *__restrict__ delta, const float *__restrict__ lse,
+                                                       float *__restrict__ rows) {
+  constexpr int C8 = D / 8;
+  const int h = blockIdx.y;
+  const int c = threadIdx.x % C8;
+  const int m = blockIdx.x * (256 / C8) + threadIdx.x / C8;   // the C8 lanes of a row exit together
+  if (m >= (BF16 ? s.Sv : s.S)) return;
+  if (BF16 && m >= s.S) {
+    *reinterpret_cast<uint4 *>(dotb + ((long long)h * s.Sv + m) * D + c * 8) = make_uint4(0u, 0u, 0u, 0u);
+    if (c == 0) *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + m)) = make_float2(0.f, 0.f);
+    return;
+  }
+  float y[8], o8[8];
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(dotb + ((long long)h * s.Sv + m) * D + c * 8);
+    const unsigned v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[2 * e] = __uint_as_float(v[e] << 16);
+      y[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  } else {
+    load_row8(dot32 + ((long long)h * s.S + m) * D + c * 8, y);
+  }
+  load_row8(ot + ((long long)h * s.S + m) * D + c * 8, o8);
+  float dl = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dl = fmaf(y[e], o8[e], dl);
+#pragma unroll
+  for (int xo = 1; xo < C8; xo <<= 1) dl += __shfl_xor(dl, xo);
+  if (c == 0) {
+    if constexpr (BF16)
+      *reinterpret_cast<float2 *>(rows + 2 * ((long long)h * s.Sv + m)) =
+          make_float2(lse[(long long)h * s.S + m] * 1.4426950408889634f, dl);
+    else
+      delta[(long long)h * s.S + m] = dl;
   }
 }
 
@@ -724,8 +742,10 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
   // position-major walk: four or more levels (where k_scatter_bwd's re-reads of
   // dO dominate), p = 2 or 4, and the coarsest range fits a work-group's span
   if ((s.p == 2 || s.p == 4) && s.L >= 4) {
-    int gw = 1, a = 0;   // rows per row group: the largest p^a <= 16 with a <= L - 1
-    while (a + 1 < s.L && gw * s.p <= 16) {
+    // rows per row group: the largest p^a <= 16 (4 at four levels, measured
+    // faster: more, shorter row groups) with a <= L - 1
+    int gw = 1, a = 0;
+    while (a + 1 < s.L && gw * s.p <= (s.L == 4 ? 4 : 16)) {
       gw *= s.p;
       ++a;
     }
@@ -733,9 +753,13 @@ hipError_t launch_scatter_bwd(const Shape &s, const void *dout, int dout_dtype, 
     const long long span = (long long)rg * gw;
     if (gw > 1 && s.pw[s.L - 1] <= span && s.L - 1 - a <= kWalkCoarse) {
       const int nwg = (int)((s.N + 1 + span - 1) / span);
-      dim3 grid((unsigned)(nwg + 1), s.BH);
-#define LH_SW(D, B, G, LG) \
-  lh::launch(k_scatter_bwd_walk<D, B, G, LG>, grid, 256, 0, st, s, nwg, dout, dout_dtype, slot, ot, dot32, dotb, delta, lse, rows)
+      dim3 grid((unsigned)nwg, s.BH);
+      dim3 gd((unsigned)(((bf ? s.Sv : s.S) + rg - 1) / rg), s.BH);
+#define LH_SW(D, B, G, LG)                                                                                     \
+  do {                                                                                                          \
+    lh::launch(k_scatter_bwd_walk<D, B, G, LG>, grid, 256, 0, st, s, dout, dout_dtype, slot, dot32, dotb);     \
+    lh::launch(k_scatter_delta<D, B>, gd, 256, 0, st, s, ot, (const float *)dot32, dotb, delta, lse, rows);   \
+  } while (0)
 #define LH_SWG(D, B)                          \
   do {                                        \
     if (s.p == 4) {                           \
