@@ -116,8 +116,10 @@ __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict_
 }
 
 constexpr int kScatterGroups = 2;   // groups of 4 positions per thread in k_scatter_hi
+constexpr int kScatterOneGroups = 1;   // groups of 4 positions per thread in k_scatter_one
 
-// p a power of two, in two passes.
+// p a power of two, in two passes (where few positions have a selected
+// level-0 entry; k_scatter_one below otherwise).
 //   k_scatter_hi   one thread per (NG groups of 4 positions, 8-element chunk):
 //                  the positions u = u0 .. u0 + 3 (u = t + 1, u0 a multiple of
 //                  4) share their entry of every level l with p^l >= 4
@@ -228,6 +230,136 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
         const int t = u0[g] + r - 1;
         if (t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
       }
+    }
+  }
+}
+
+// p a power of two, in one pass: the coarse part of k_scatter_hi (the same
+// groups, lookups and rows), plus the slots of the group's four level-0
+// entries, looked up with the coarser ones.  Each group's coarser levels are
+// summed once in exact fixed point (per pair at P2); then the level-0 rows of
+// the thread's selected positions are loaded, into the registers the coarser
+// rows held, and every position is written once with its full sum.  On the
+// large-value path (some |x| >= 2^18) the coarser rows are read again and the
+// int64 sum formed, as fixed_out does.
+template <int D, int LM, bool P2>
+__global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restrict__ slot,
+                                                     const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
+  constexpr int C8 = D / 8;
+  constexpr int NG = kScatterOneGroups;
+  constexpr int GPP = 256 / C8;    // groups per pass of the work-group
+  constexpr int NPR = P2 ? 2 : 1;  // coarse sums per group
+  const int h = blockIdx.y;
+  const int c = threadIdx.x % C8;
+  const int lg = __builtin_ctz(s.p);
+  const int *sl = slot + (long long)h * s.P;
+  const float *ob = ot + (long long)h * s.S * D + c * 8;
+  int u0[NG], mh[NG][LM], m1[NG], m0[NG][4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    u0[g] = 4 * (blockIdx.x * (GPP * NG) + g * GPP + threadIdx.x / C8);
+#pragma unroll
+    for (int l = 0; l < LM; ++l) {
+      mh[g][l] = -1;
+      if (l >= 1 && l < s.L && u0[g] <= s.N) {
+        const int i = (u0[g] >> (l * lg)) - 1;
+        if (i >= 0) mh[g][l] = sl[s.off[l] + i];
+      }
+    }
+    m1[g] = -1;
+    if (P2 && s.L > 1 && u0[g] + 2 <= s.N) m1[g] = sl[s.off[1] + (u0[g] >> 1)];   // i = (u0 + 2) / 2 - 1
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = u0[g] + r - 1;
+      m0[g][r] = (t >= 0 && t < s.N) ? sl[t] : -1;
+    }
+  }
+  // coarse sums: A[g][pr] = sum of RNE(x 2^32) over the coarser levels of the
+  // group (pair pr at P2), exact in fp64 unless big[g]
+  double A[NG][NPR][8];
+  bool big[NG];
+  {
+    float xs[NG][LM][8], x1[P2 ? NG : 1][8];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int l = 1; l < LM; ++l)
+        if (mh[g][l] >= 0) load_row8(ob + (long long)mh[g][l] * D, xs[g][l]);
+      if constexpr (P2)
+        if (m1[g] >= 0) load_row8(ob + (long long)m1[g] * D, x1[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      big[g] = false;
+      double sh[8];   // levels 2 .. (shared by both pairs at P2), then level 1
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh[e] = 0.0;
+#pragma unroll
+      for (int l = 2; l < LM; ++l) {
+        if (mh[g][l] < 0) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          big[g] |= !(fabsf(xs[g][l][e]) < 262144.f);
+          sh[e] += (double)rintf(xs[g][l][e] * 4294967296.0f);
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < NPR; ++pr) {
+        const bool has1 = pr == 0 ? mh[g][1] >= 0 : m1[g] >= 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          A[g][pr][e] = sh[e];
+          if (has1) {
+            const float x = pr == 0 ? xs[g][1][e] : x1[P2 ? g : 0][e];
+            big[g] |= !(fabsf(x) < 262144.f);
+            A[g][pr][e] += (double)rintf(x * 4294967296.0f);
+          }
+        }
+      }
+    }
+  }
+  // level-0 rows of the selected positions, then every position once
+  float x0[NG][4][8];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (m0[g][r] >= 0) load_row8(ob + (long long)m0[g][r] * D, x0[g][r]);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = u0[g] + r - 1;
+      if (t < 0 || t >= s.N) continue;
+      const int pr = P2 ? (r >> 1) : 0;
+      bool bg = big[g];
+      double a[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = A[g][pr][e];
+        if (m0[g][r] >= 0) {
+          bg |= !(fabsf(x0[g][r][e]) < 262144.f);
+          a[e] += (double)rintf(x0[g][r][e] * 4294967296.0f);
+        }
+      }
+      float q[8];
+      if (!bg) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = (float)(a[e] * 2.3283064365386963e-10);
+      } else {
+        // int64 path: the position's terms again, from memory
+        long long b[8];
+        for (int e = 0; e < 8; ++e) b[e] = m0[g][r] >= 0 ? to_fixed(x0[g][r][e]) : 0;
+        for (int l = 1; l < LM; ++l) {
+          const int m = (P2 && l == 1 && pr == 1) ? m1[g] : mh[g][l];
+          if (m < 0) continue;
+          float x[8];
+          load_row8(ob + (long long)m * D, x);
+          for (int e = 0; e < 8; ++e) b[e] += to_fixed(x[e]);
+        }
+        for (int e = 0; e < 8; ++e) q[e] = from_fixed(b[e]);
+      }
+      store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
     }
   }
 }
@@ -703,13 +835,23 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
                           int o_dtype, hipStream_t st) {
   const int per = 256 / (s.d / 8);   // positions (or groups of 4 positions) per pass of a work-group
   if (s.p >= 2 && (s.p & (s.p - 1)) == 0 && (s.p >= 4 || (s.N & 1) == 0)) {
-    const int gpb = per * kScatterGroups;
+    // One pass where level-0 entries are dense, two passes elsewhere.  Their
+    // density follows the budget; measured at N = 98,304 the one pass is as
+    // fast from Bsel = N / 4 on (L = 3, p = 4, k = 3,072) and faster beyond
+    // (k = 6,144: 64% vs 49% of the HBM peak), two passes below (512K, where
+    // 3% of the positions have a level-0 entry: 0.28 vs 0.39 ms).
+    const bool one = 4LL * s.Bsel >= s.N;
+    const int gpb = per * (one ? kScatterOneGroups : kScatterGroups);
     dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // groups u0 = 0, 4, ..., <= N
     dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);
 #define LH_SC(D, LM, P2)                                                                             \
   do {                                                                                               \
-    lh::launch(k_scatter_hi<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                  \
-    lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);               \
+    if (one) {                                                                                       \
+      lh::launch(k_scatter_one<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);               \
+    } else {                                                                                         \
+      lh::launch(k_scatter_hi<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                \
+      lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);             \
+    }                                                                                                \
   } while (0)
 #define LH_SCL(D, P2)                   \
   do {                                  \

@@ -269,15 +269,17 @@ def test_deterministic(lh):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
 
 
-@pytest.mark.parametrize("N,L,p", [(1024, 3, 4), (1944, 3, 3), (1024, 4, 2)])
-def test_scatter_large_values(lh, N, L, p):
+@pytest.mark.parametrize("N,L,p,k", [(1024, 3, 4, 64), (1024, 3, 4, 8), (1944, 3, 3, 64), (1024, 4, 2, 64),
+                                     (1024, 4, 2, 8)])
+def test_scatter_large_values(lh, N, L, p, k):
     """Sub-sequence outputs of magnitude >= 2^18 make the scatter form its
     fixed-point sums in int64 instead of fp64; the result stays bit-exact.
     V is scaled by 2^20 on half of the positions, so both forms occur.  p = 4,
     p = 2 and p = 3 take the scatter's thread layouts (groups of four positions
     sharing their coarser entries, the same with one level-1 entry per pair,
-    one position per thread)."""
-    cfg = synth.config("tiny", N=N, L=L, p=p)
+    one position per thread); k = 64 (budget >= N / 4) the one-pass kernel,
+    k = 8 the two passes."""
+    cfg = synth.config("tiny", N=N, L=L, p=p, k=k)
     inp = synth.make_inputs(cfg)
     N, L, p = cfg["N"], cfg["L"], cfg["p"]
     inp["v"] = inp["v"].copy()
