@@ -115,19 +115,20 @@ __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict_
   store_row8(o, o_dtype, ((long long)h * s.N + (u - 1)) * D + c * 8, q);
 }
 
-constexpr int kScatterGroups = 2;   // groups of 4 positions per thread in k_scatter_hi
 constexpr int kScatterOneGroups = 1;   // groups of 4 positions per thread in k_scatter_one
 
 // p a power of two, in two passes (where few positions have a selected
 // level-0 entry; k_scatter_one below otherwise).
-//   k_scatter_hi   one thread per (NG groups of 4 positions, 8-element chunk):
-//                  the positions u = u0 .. u0 + 3 (u = t + 1, u0 a multiple of
-//                  4) share their entry of every level l with p^l >= 4
-//                  (i = (u0 >> l log2 p) - 1), so a group needs one slot lookup
-//                  and one row per such level; at p = 2 (P2) level 1 has one
-//                  entry per pair of the group's positions, two rows.  All
-//                  lookups of the thread's groups are issued first, then all
-//                  rows.  Writes every position's sum over its coarser levels.
+//   k_scatter_hi   one thread per (8 positions u = u0 .. u0 + 7, u = t + 1, u0
+//                  a multiple of 8; 8-element chunk).  Every level with
+//                  p^l >= 8 has one entry for all eight (i = (u0 >> l log2 p)
+//                  - 1), looked up and read once; p^l = 4 has one per group of
+//                  four and, at p = 2 (P2), p^l = 2 one per pair.  All lookups
+//                  are issued first, then all rows; each position's sum is
+//                  fixed_out's, formed with the shared levels' terms first
+//                  (every partial sum is an exact integer in fp64, so the value
+//                  is the same), on the same large-value condition.  Writes
+//                  every position's sum over its coarser levels.
 //   k_scatter_lo   one thread per (gathered row, 8-element chunk); rows of
 //                  level 0 (a few percent of them) rewrite their position's
 //                  output with the full sum, their own row included.
@@ -171,72 +172,11 @@ __device__ __forceinline__ void fixed_out(const float (&xs)[LM][8], const bool (
   }
 }
 
-template <int D, int LM, bool P2>
-__global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restrict__ slot,
-                                                    const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
-  constexpr int C8 = D / 8;
-  constexpr int NG = kScatterGroups;
-  constexpr int GPP = 256 / C8;   // groups per pass of the work-group
-  const int h = blockIdx.y;
-  const int c = threadIdx.x % C8;
-  const int lg = __builtin_ctz(s.p);
-  const int *sl = slot + (long long)h * s.P;
-  const float *ob = ot + (long long)h * s.S * D + c * 8;
-  // mh[g][l]: the group's entry of level l (at P2, level 1: its first pair's);
-  // m1[g]: at P2, the level-1 entry of its second pair (u0 + 2, u0 + 3)
-  int u0[NG], mh[NG][LM], m1[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    u0[g] = 4 * (blockIdx.x * (GPP * NG) + g * GPP + threadIdx.x / C8);
-#pragma unroll
-    for (int l = 0; l < LM; ++l) {
-      mh[g][l] = -1;
-      if (l >= 1 && l < s.L && u0[g] <= s.N) {
-        const int i = (u0[g] >> (l * lg)) - 1;
-        if (i >= 0) mh[g][l] = sl[s.off[l] + i];
-      }
-    }
-    m1[g] = -1;
-    if (P2 && s.L > 1 && u0[g] + 2 <= s.N) m1[g] = sl[s.off[1] + (u0[g] >> 1)];   // i = (u0 + 2) / 2 - 1
-  }
-  float xs[NG][LM][8], x1[P2 ? NG : 1][8];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-#pragma unroll
-    for (int l = 1; l < LM; ++l)
-      if (mh[g][l] >= 0) load_row8(ob + (long long)mh[g][l] * D, xs[g][l]);
-    if constexpr (P2)
-      if (m1[g] >= 0) load_row8(ob + (long long)m1[g] * D, x1[g]);
-  }
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    bool has[LM];
-#pragma unroll
-    for (int l = 0; l < LM; ++l) has[l] = l >= 1 && mh[g][l] >= 0;
-    float q[8];
-    fixed_out<LM>(xs[g], has, q);
-#pragma unroll
-    for (int r = 0; r < (P2 ? 2 : 4); ++r) {
-      const int t = u0[g] + r - 1;
-      if (t >= 0 && t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
-    }
-    if constexpr (P2) {   // the second pair: its own level-1 row
-      has[1] = m1[g] >= 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[g][1][e] = x1[g][e];
-      fixed_out<LM>(xs[g], has, q);
-#pragma unroll
-      for (int r = 2; r < 4; ++r) {
-        const int t = u0[g] + r - 1;
-        if (t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
-      }
-    }
-  }
-}
-
-// p a power of two, in one pass: the coarse part of k_scatter_hi (the same
-// groups, lookups and rows), plus the slots of the group's four level-0
-// entries, looked up with the coarser ones.  Each group's coarser levels are
+// p a power of two, in one pass: one thread per (group of 4 positions u =
+// u0 .. u0 + 3, u0 a multiple of 4; 8-element chunk).  The group shares its
+// entry of every level with p^l >= 4 (one per pair at level 1 at P2); those
+// slots are looked up together with the slots of the group's four level-0
+// entries.  Each group's coarser levels are
 // summed once in exact fixed point (per pair at P2); then the level-0 rows of
 // the thread's selected positions are loaded, into the registers the coarser
 // rows held, and every position is written once with its full sum.  On the
@@ -360,6 +300,95 @@ __global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restr
         for (int e = 0; e < 8; ++e) q[e] = from_fixed(b[e]);
       }
       store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, q);
+    }
+  }
+}
+
+template <int D, int LM, bool P2>
+__global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restrict__ slot,
+                                                     const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
+  constexpr int C8 = D / 8;
+  constexpr int UPP = 256 / C8;   // 8-position units per work-group
+  const int h = blockIdx.y;
+  const int c = threadIdx.x % C8;
+  const int lg = __builtin_ctz(s.p);
+  const int *sl = slot + (long long)h * s.P;
+  const float *ob = ot + (long long)h * s.S * D + c * 8;
+  const int u0 = 8 * (blockIdx.x * UPP + threadIdx.x / C8);
+  if (u0 > s.N) return;
+  // the level with p^l = 4 (l4: 2 at P2, 1 at p = 4, none at p >= 8), the
+  // level with p^l = 2 (level 1 at P2), and the shared levels l >= ls
+  const int l4 = P2 ? 2 : (s.p == 4 ? 1 : 0);
+  const int ls = P2 ? 3 : l4 + 1;
+  auto look = [&](int l, int u) {
+    if (l < 1 || l >= s.L || u > s.N) return -1;
+    const int i = (u >> (l * lg)) - 1;
+    return i >= 0 ? sl[s.off[l] + i] : -1;
+  };
+  int mg[2], mp[P2 ? 4 : 1], mc[LM];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) mg[g] = l4 > 0 ? look(l4, u0 + 4 * g) : -1;
+#pragma unroll
+  for (int q = 0; q < (P2 ? 4 : 1); ++q) mp[q] = P2 ? look(1, u0 + 2 * q) : -1;
+#pragma unroll
+  for (int l = 0; l < LM; ++l) mc[l] = l >= ls ? look(l, u0) : -1;
+  float xg[2][8], xp[P2 ? 4 : 1][8], xc[LM][8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+    if (mg[g] >= 0) load_row8(ob + (long long)mg[g] * D, xg[g]);
+#pragma unroll
+  for (int q = 0; q < (P2 ? 4 : 1); ++q)
+    if (mp[q] >= 0) load_row8(ob + (long long)mp[q] * D, xp[q]);
+#pragma unroll
+  for (int l = 1; l < LM; ++l)
+    if (mc[l] >= 0) load_row8(ob + (long long)mc[l] * D, xc[l]);
+  auto add = [&](const float (&x)[8], double (&a)[8], bool &bg) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bg |= !(fabsf(x[e]) < 262144.f);
+      a[e] += (double)rintf(x[e] * 4294967296.0f);
+    }
+  };
+  bool big = false;
+  double A[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) A[e] = 0.0;
+#pragma unroll
+  for (int l = 1; l < LM; ++l)
+    if (mc[l] >= 0) add(xc[l], A, big);
+  // units of positions with the same entries: pairs at P2, groups otherwise
+  constexpr int UN = P2 ? 4 : 2;
+  constexpr int UW = 8 / UN;
+#pragma unroll
+  for (int k = 0; k < UN; ++k) {
+    const int uk = u0 + UW * k;
+    if (uk > s.N) break;
+    const int g = P2 ? k >> 1 : k;
+    bool bg = big;
+    double a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = A[e];
+    if (mg[g] >= 0) add(xg[g], a, bg);
+    if constexpr (P2)
+      if (mp[k] >= 0) add(xp[k], a, bg);
+    float qv[8];
+    if (!bg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = (float)(a[e] * 2.3283064365386963e-10);
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        long long b = mg[g] >= 0 ? to_fixed(xg[g][e]) : 0;
+        if constexpr (P2)
+          if (mp[k] >= 0) b += to_fixed(xp[k][e]);
+        for (int l = 1; l < LM; ++l)
+          if (mc[l] >= 0) b += to_fixed(xc[l][e]);
+        qv[e] = from_fixed(b);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < UW; ++r) {
+      const int t = uk + r - 1;
+      if (t >= 0 && t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, qv);
     }
   }
 }
@@ -841,15 +870,16 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
     // (k = 6,144: 64% vs 49% of the HBM peak), two passes below (512K, where
     // 3% of the positions have a level-0 entry: 0.28 vs 0.39 ms).
     const bool one = 4LL * s.Bsel >= s.N;
-    const int gpb = per * (one ? kScatterOneGroups : kScatterGroups);
-    dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // groups u0 = 0, 4, ..., <= N
-    dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);
+    const int gpb = per * kScatterOneGroups;
+    dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // k_scatter_one: groups u0 = 0, 4, ..., <= N
+    dim3 g8((unsigned)((s.N / 8 + 1 + per - 1) / per), s.BH);     // k_scatter_hi: units u0 = 0, 8, ..., <= N
+    dim3 glo((unsigned)((s.S + per - 1) / per), s.BH);            // k_scatter_lo: gathered rows
 #define LH_SC(D, LM, P2)                                                                             \
   do {                                                                                               \
     if (one) {                                                                                       \
       lh::launch(k_scatter_one<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);               \
     } else {                                                                                         \
-      lh::launch(k_scatter_hi<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);                \
+      lh::launch(k_scatter_hi<D, LM, P2>, g8, 256, 0, st, s, slot, ot, o, o_dtype);                \
       lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);             \
     }                                                                                                \
   } while (0)
