@@ -117,18 +117,18 @@ __global__ __launch_bounds__(256) void k_scatter(Shape s, const int *__restrict_
 
 constexpr int kScatterOneGroups = 1;   // groups of 4 positions per thread in k_scatter_one
 
-// p a power of two, in two passes (where few positions have a selected
+// p a power of two >= 4, in two passes (where few positions have a selected
 // level-0 entry; k_scatter_one below otherwise).
 //   k_scatter_hi   one thread per (8 positions u = u0 .. u0 + 7, u = t + 1, u0
 //                  a multiple of 8; 8-element chunk).  Every level with
 //                  p^l >= 8 has one entry for all eight (i = (u0 >> l log2 p)
-//                  - 1), looked up and read once; p^l = 4 has one per group of
-//                  four and, at p = 2 (P2), p^l = 2 one per pair.  All lookups
-//                  are issued first, then all rows; each position's sum is
-//                  fixed_out's, formed with the shared levels' terms first
-//                  (every partial sum is an exact integer in fp64, so the value
-//                  is the same), on the same large-value condition.  Writes
-//                  every position's sum over its coarser levels.
+//                  - 1), looked up and read once; at p = 4 level 1 has one per
+//                  group of four.  All lookups are issued first, then all rows;
+//                  each position's sum is fixed_out's, formed with the shared
+//                  levels' terms first (every partial sum is an exact integer
+//                  in fp64, so the value is the same), on the same large-value
+//                  condition.  Writes every position's sum over its coarser
+//                  levels.
 //   k_scatter_lo   one thread per (gathered row, 8-element chunk); rows of
 //                  level 0 (a few percent of them) rewrite their position's
 //                  output with the full sum, their own row included.
@@ -176,12 +176,11 @@ __device__ __forceinline__ void fixed_out(const float (&xs)[LM][8], const bool (
 // u0 .. u0 + 3, u0 a multiple of 4; 8-element chunk).  The group shares its
 // entry of every level with p^l >= 4 (one per pair at level 1 at P2); those
 // slots are looked up together with the slots of the group's four level-0
-// entries.  Each group's coarser levels are
-// summed once in exact fixed point (per pair at P2); then the level-0 rows of
-// the thread's selected positions are loaded, into the registers the coarser
-// rows held, and every position is written once with its full sum.  On the
-// large-value path (some |x| >= 2^18) the coarser rows are read again and the
-// int64 sum formed, as fixed_out does.
+// entries, and the coarser rows and the selected level-0 rows are then loaded
+// together.  The coarser levels are summed once per group (per pair at P2) in
+// exact fixed point, each position adds its level-0 term, and every position is
+// written once with its full sum.  On the large-value path (some |x| >= 2^18)
+// the coarser rows are read again and the int64 sum formed, as fixed_out does.
 template <int D, int LM, bool P2>
 __global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restrict__ slot,
                                                      const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
@@ -214,6 +213,12 @@ __global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restr
       m0[g][r] = (t >= 0 && t < s.N) ? sl[t] : -1;
     }
   }
+  float x0[NG][4][8];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (m0[g][r] >= 0) load_row8(ob + (long long)m0[g][r] * D, x0[g][r]);
   // coarse sums: A[g][pr] = sum of RNE(x 2^32) over the coarser levels of the
   // group (pair pr at P2), exact in fp64 unless big[g]
   double A[NG][NPR][8];
@@ -258,13 +263,6 @@ __global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restr
       }
     }
   }
-  // level-0 rows of the selected positions, then every position once
-  float x0[NG][4][8];
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (m0[g][r] >= 0) load_row8(ob + (long long)m0[g][r] * D, x0[g][r]);
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
 #pragma unroll
@@ -304,9 +302,9 @@ __global__ __launch_bounds__(256) void k_scatter_one(Shape s, const int *__restr
   }
 }
 
-template <int D, int LM, bool P2>
+template <int D, int LM>
 __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restrict__ slot,
-                                                     const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
+                                                    const float *__restrict__ ot, void *__restrict__ o, int o_dtype) {
   constexpr int C8 = D / 8;
   constexpr int UPP = 256 / C8;   // 8-position units per work-group
   const int h = blockIdx.y;
@@ -316,29 +314,24 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
   const float *ob = ot + (long long)h * s.S * D + c * 8;
   const int u0 = 8 * (blockIdx.x * UPP + threadIdx.x / C8);
   if (u0 > s.N) return;
-  // the level with p^l = 4 (l4: 2 at P2, 1 at p = 4, none at p >= 8), the
-  // level with p^l = 2 (level 1 at P2), and the shared levels l >= ls
-  const int l4 = P2 ? 2 : (s.p == 4 ? 1 : 0);
-  const int ls = P2 ? 3 : l4 + 1;
+  // level 1 at p = 4 has one entry per group of four; the levels l >= ls one
+  // for all eight positions
+  const int l4 = s.p == 4 ? 1 : 0;
+  const int ls = l4 + 1;
   auto look = [&](int l, int u) {
     if (l < 1 || l >= s.L || u > s.N) return -1;
     const int i = (u >> (l * lg)) - 1;
     return i >= 0 ? sl[s.off[l] + i] : -1;
   };
-  int mg[2], mp[P2 ? 4 : 1], mc[LM];
+  int mg[2], mc[LM];
 #pragma unroll
   for (int g = 0; g < 2; ++g) mg[g] = l4 > 0 ? look(l4, u0 + 4 * g) : -1;
 #pragma unroll
-  for (int q = 0; q < (P2 ? 4 : 1); ++q) mp[q] = P2 ? look(1, u0 + 2 * q) : -1;
-#pragma unroll
   for (int l = 0; l < LM; ++l) mc[l] = l >= ls ? look(l, u0) : -1;
-  float xg[2][8], xp[P2 ? 4 : 1][8], xc[LM][8];
+  float xg[2][8], xc[LM][8];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
     if (mg[g] >= 0) load_row8(ob + (long long)mg[g] * D, xg[g]);
-#pragma unroll
-  for (int q = 0; q < (P2 ? 4 : 1); ++q)
-    if (mp[q] >= 0) load_row8(ob + (long long)mp[q] * D, xp[q]);
 #pragma unroll
   for (int l = 1; l < LM; ++l)
     if (mc[l] >= 0) load_row8(ob + (long long)mc[l] * D, xc[l]);
@@ -356,21 +349,15 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
 #pragma unroll
   for (int l = 1; l < LM; ++l)
     if (mc[l] >= 0) add(xc[l], A, big);
-  // units of positions with the same entries: pairs at P2, groups otherwise
-  constexpr int UN = P2 ? 4 : 2;
-  constexpr int UW = 8 / UN;
 #pragma unroll
-  for (int k = 0; k < UN; ++k) {
-    const int uk = u0 + UW * k;
-    if (uk > s.N) break;
-    const int g = P2 ? k >> 1 : k;
+  for (int g = 0; g < 2; ++g) {
+    const int ug = u0 + 4 * g;
+    if (ug > s.N) break;
     bool bg = big;
     double a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = A[e];
     if (mg[g] >= 0) add(xg[g], a, bg);
-    if constexpr (P2)
-      if (mp[k] >= 0) add(xp[k], a, bg);
     float qv[8];
     if (!bg) {
 #pragma unroll
@@ -378,16 +365,14 @@ __global__ __launch_bounds__(256) void k_scatter_hi(Shape s, const int *__restri
     } else {
       for (int e = 0; e < 8; ++e) {
         long long b = mg[g] >= 0 ? to_fixed(xg[g][e]) : 0;
-        if constexpr (P2)
-          if (mp[k] >= 0) b += to_fixed(xp[k][e]);
         for (int l = 1; l < LM; ++l)
           if (mc[l] >= 0) b += to_fixed(xc[l][e]);
         qv[e] = from_fixed(b);
       }
     }
 #pragma unroll
-    for (int r = 0; r < UW; ++r) {
-      const int t = uk + r - 1;
+    for (int r = 0; r < 4; ++r) {
+      const int t = ug + r - 1;
       if (t >= 0 && t < s.N) store_row8(o, o_dtype, ((long long)h * s.N + t) * D + c * 8, qv);
     }
   }
@@ -865,11 +850,13 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
   const int per = 256 / (s.d / 8);   // positions (or groups of 4 positions) per pass of a work-group
   if (s.p >= 2 && (s.p & (s.p - 1)) == 0 && (s.p >= 4 || (s.N & 1) == 0)) {
     // One pass where level-0 entries are dense, two passes elsewhere.  Their
-    // density follows the budget; measured at N = 98,304 the one pass is as
-    // fast from Bsel = N / 4 on (L = 3, p = 4, k = 3,072) and faster beyond
-    // (k = 6,144: 64% vs 49% of the HBM peak), two passes below (512K, where
-    // 3% of the positions have a level-0 entry: 0.28 vs 0.39 ms).
-    const bool one = 4LL * s.Bsel >= s.N;
+    // density follows the budget.  Measured at N = 98,304: at p >= 4 the one
+    // pass is faster from Bsel = N / 4 on (L = 3, k = 3,072 / 6,144: 56% / 69%
+    // of the HBM peak vs 53% / 48%), slower below (k = 1,536: 49% vs 57%; 512K,
+    // where 3% of the positions have a level-0 entry: 0.39 vs 0.28 ms); at
+    // p = 2 at every budget measured (k = 1,536 / 4,096: 64% / 69% vs 59% /
+    // 54%), so p = 2 always takes it.
+    const bool one = s.p == 2 || 4LL * s.Bsel >= s.N;
     const int gpb = per * kScatterOneGroups;
     dim3 grid((unsigned)((s.N / 4 + 1 + gpb - 1) / gpb), s.BH);   // k_scatter_one: groups u0 = 0, 4, ..., <= N
     dim3 g8((unsigned)((s.N / 8 + 1 + per - 1) / per), s.BH);     // k_scatter_hi: units u0 = 0, 8, ..., <= N
@@ -879,7 +866,7 @@ hipError_t launch_scatter(const Shape &s, const int *slot, const int *coords, co
     if (one) {                                                                                       \
       lh::launch(k_scatter_one<D, LM, P2>, grid, 256, 0, st, s, slot, ot, o, o_dtype);               \
     } else {                                                                                         \
-      lh::launch(k_scatter_hi<D, LM, P2>, g8, 256, 0, st, s, slot, ot, o, o_dtype);                \
+      lh::launch(k_scatter_hi<D, LM>, g8, 256, 0, st, s, slot, ot, o, o_dtype);                     \
       lh::launch(k_scatter_lo<D, LM>, glo, 256, 0, st, s, slot, coords, ot, o, o_dtype);             \
     }                                                                                                \
   } while (0)

@@ -149,6 +149,7 @@ def test_tiny_L1_dense(lh):
     (3328, 5, 4, 16, 1, 2),     # five levels, p = 4: coarsest windows split over row-groups, ragged last work-group
     (3240, 5, 3, 10, 1, 1),     # five levels, p = 3: coarsest windows walked whole
     (1944, 3, 3, 20, 1, 2),     # p = 3: a pooling factor that is not a power of two
+    (4096, 3, 8, 12, 1, 1),     # p = 8: both coarser levels shared by eight positions in the scatter
 ])
 def test_shapes_fp32(lh, N, L, p, k, B, H):
     cfg = synth.config("tiny", N=N, L=L, p=p, k=k, B=B, H=H, recipe="mod97x4")
@@ -269,16 +270,17 @@ def test_deterministic(lh):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), n
 
 
-@pytest.mark.parametrize("N,L,p,k", [(1024, 3, 4, 64), (1024, 3, 4, 8), (1944, 3, 3, 64), (1024, 4, 2, 64),
-                                     (1024, 4, 2, 8)])
+@pytest.mark.parametrize("N,L,p,k", [(1024, 3, 4, 64), (1024, 3, 4, 8), (1024, 3, 8, 4), (1944, 3, 3, 64),
+                                     (1024, 4, 2, 64)])
 def test_scatter_large_values(lh, N, L, p, k):
     """Sub-sequence outputs of magnitude >= 2^18 make the scatter form its
     fixed-point sums in int64 instead of fp64; the result stays bit-exact.
     V is scaled by 2^20 on half of the positions, so both forms occur.  p = 4,
     p = 2 and p = 3 take the scatter's thread layouts (groups of four positions
     sharing their coarser entries, the same with one level-1 entry per pair,
-    one position per thread); k = 64 (budget >= N / 4) the one-pass kernel,
-    k = 8 the two passes."""
+    one position per thread).  At p >= 4 a budget >= N / 4 (k = 64) takes the
+    one-pass kernel and a smaller one the two passes, whose coarse pass has a
+    per-group level at p = 4 and none at p = 8; p = 2 always takes one pass."""
     cfg = synth.config("tiny", N=N, L=L, p=p, k=k)
     inp = synth.make_inputs(cfg)
     N, L, p = cfg["N"], cfg["L"], cfg["p"]
