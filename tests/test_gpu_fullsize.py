@@ -19,7 +19,9 @@ heads of each workload:
                                                 multipliers <= 4); the 1M Zipf workload
                                                 scales both Q and K by up to 16, logits
                                                 reach |z| ~ 1e2-1e3, and a bf16 rounding of
-                                                a pooled row then moves a logit by O(1)
+                                                a pooled row then moves a logit by O(1):
+                                                there it is held under 0.25 (measured
+                                                0.10-0.13)
 and for the backward, properties that hold at any size: finite gradients,
 exact scaling by 2 of dO, bit-equal repeat.
 """
@@ -103,6 +105,12 @@ def _check_full_head(cfg, inp, run, lh, h):
     assert errs["bf16"] <= 2e-2
     if cfg["recipe"] != "zipf":
         assert errs[None] <= 2e-2
+    else:
+        # logits up to |z| ~ 1e3: one bf16 rounding of a pooled row (unit
+        # roundoff 2^-8) moves a logit by O(1), so the pure-fp64 pyramid is
+        # a different softmax; measured 0.10-0.13, held under 0.25 so that the
+        # sensitivity stays a checked number
+        assert errs[None] <= 0.25
 
 
 def _make_inputs_verbose(cfg, with_do=False):
