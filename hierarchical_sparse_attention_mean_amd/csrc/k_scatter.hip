@@ -13,13 +13,15 @@
 // i = floor((t+1) / p^l) - 1, so each output element pulls its <= L
 // contributions and owns its accumulator.
 //
-// When p is a power of two the scatter runs in two passes (coarser levels for
-// every position, then the few positions with a selected level-0 entry); see
-// k_scatter_hi / k_scatter_lo.
+// When p is a power of two the scatter groups positions that share their
+// coarser entries: in one pass (k_scatter_one) where level-0 entries are dense,
+// otherwise in two (coarser levels for every position, then the few positions
+// with a selected level-0 entry; k_scatter_hi / k_scatter_lo).
 //
 // Adjoints (Sec. 3.2: gradients flow through scatter, attention, gather and
 // pool; the selection is frozen):
-//   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m;
+//   k_scatter_bwd  dO~_m = sum of dO_t over the scatter range of entry m
+//                  (k_scatter_bwd_walk + k_scatter_delta at four levels or more);
 //   k_pool_bwd     dX_t = sum_l [entry (l, floor(t/p^l)) selected] dX~_slot / p^l
 //                  for X in {Q, K, V} (gather adjoint fused with pool adjoint).
 #include <type_traits>
