@@ -101,6 +101,15 @@ def test_backward_shapes(lh):
     _run_bwd(lh, synth.config("tiny", N=4096, L=4, p=4, k=16, H=1), heads=[0])
 
 
+def test_backward_degenerate_shapes(lh):
+    """Smallest shapes: one coarsest window (N = 16, S = 9), three heads of
+    N = 6 at p = 2 (S = 5), and a bf16 sub-sequence shorter than one 32-row
+    attention tile (N = 64, S = 28, rows padded to Sv = 64)."""
+    _run_bwd(lh, synth.config("tiny", N=16, L=3, p=4, k=1, H=1), heads=[0])
+    _run_bwd(lh, synth.config("tiny", N=6, L=2, p=2, k=1, H=3), heads=[0, 2])
+    _run_bwd(lh, synth.config("bwd8k", N=64, L=3, p=4, k=3, H=1), heads=[0])
+
+
 @pytest.mark.parametrize("over", [
     dict(N=2048, H=2, d=64),                  # bf16 MFMA backward at d = 64
     dict(N=2048, L=4, p=2, k=16, H=1, d=64),  # p = 2: the one-position-per-thread scatter and pool adjoints

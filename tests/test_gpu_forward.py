@@ -150,6 +150,9 @@ def test_tiny_L1_dense(lh):
     (3240, 5, 3, 10, 1, 1),     # five levels, p = 3: coarsest windows walked whole
     (1944, 3, 3, 20, 1, 2),     # p = 3: a pooling factor that is not a power of two
     (4096, 3, 8, 12, 1, 1),     # p = 8: both coarser levels shared by eight positions in the scatter
+    (16, 3, 4, 1, 1, 1),        # one coarsest window (S = 9)
+    (4, 2, 4, 0, 1, 1),         # N = p and k = 0: the single coarsest entry (S = 1)
+    (6, 2, 2, 1, 1, 3),         # N = 6, p = 2, three heads (B*H not a multiple of 8)
 ])
 def test_shapes_fp32(lh, N, L, p, k, B, H):
     cfg = synth.config("tiny", N=N, L=L, p=p, k=k, B=B, H=H, recipe="mod97x4")
@@ -161,6 +164,7 @@ def test_shapes_fp32(lh, N, L, p, k, B, H):
     (4096, 5, 4, 8, 128),    # five levels, p = 4 (groups of four positions in the scatter)
     (2048, 6, 4, 4, 128),    # six levels: the widest level templates
     (1024, 8, 2, 4, 64),     # eight levels, p = 2
+    (64, 3, 4, 3, 128),      # S = 28: less than one 32-row attention tile, rows padded to Sv = 64
 ])
 def test_shapes_bf16(lh, N, L, p, k, d):
     """bf16 storage at the level counts the bf16 workloads do not reach, stage by stage."""
