@@ -148,6 +148,7 @@ def test_tiny_L1_dense(lh):
     (4096, 5, 2, 200, 1, 1),    # five levels
     (3328, 5, 4, 16, 1, 2),     # five levels, p = 4: coarsest windows split over row-groups, ragged last work-group
     (3240, 5, 3, 10, 1, 1),     # five levels, p = 3: coarsest windows walked whole
+    (4096, 5, 8, 4, 1, 1),      # five levels, p = 8: one coarsest window walked by eight row-groups
     (1944, 3, 3, 20, 1, 2),     # p = 3: a pooling factor that is not a power of two
     (4096, 3, 8, 12, 1, 1),     # p = 8: both coarser levels shared by eight positions in the scatter
     (16, 3, 4, 1, 1, 1),        # one coarsest window (S = 9)
